@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs for one decode step of attention over a KV cache.
+
+This module only draws numbers and lays them out; it holds none of the
+attention arithmetic, no slot mapping and no masking.  Both the oracle side
+(tests) and the library side (tests, bench) take their inputs from here.
+
+Workload shapes follow the decode settings the source pages discuss:
+  * a 7B-style model with 32 query / 32 KV heads of width 128 in fp16
+    ("KV cache math" section of the nextadmin.net lesson on the KV cache and
+    Flash Attention, and the "KV-cache memory bottleneck" section of the
+    dothoosh.com StreamingLLM article);
+  * speculative verification of 1 accepted + 4 draft tokens against a GQA
+    model (dothoosh.com speculative-decoding article, "parallel verification"
+    and "verify phase");
+  * a StreamingLLM cache of 4 sink tokens plus a 4,092-token window (StreamingLLM
+    article, "The StreamingLLM solution");
+  * a 100,000-token context paged in 16-token blocks through a page table
+    (lesson, "PagedAttention - the KV cache as virtual memory").
+
+Draw order (fixed, so a seed names one input set): integer structure first
+(sequence lengths, block permutation), then Q, K, V as float32 standard
+normals, then the value scale (and the optional boost of K at position 0),
+then the cast to the storage dtype.
+
+Layouts (row-major, head_dim innermost):
+  q, out            [batch, q_len, num_q_heads, head_dim]
+  contiguous / ring [batch, capacity, num_kv_heads, head_dim]
+  paged             [num_blocks, block_size, num_kv_heads, head_dim]
+  block_table       int32 [batch, capacity // block_size]
+  seq_lens          int32 [batch]
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Case:
+    name: str
+    seed: int
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str                      # "f32" | "f16" | "bf16"
+    cache_mode: str                 # "contiguous" | "paged" | "ring"
+    capacity: int                   # slots per sequence (paged: blocks_per_seq * block_size)
+    q_len: int = 1
+    mask_mode: str = "causal"       # "causal" | "sink_window"
+    n_sink: int = 0
+    window: int = 0
+    block_size: int = 16
+    num_blocks: int = 0             # paged pool size
+    seq_lens: Optional[Tuple[int, ...]] = None      # fixed lengths, or
+    seq_len_range: Optional[Tuple[int, int]] = None  # inclusive uniform integer range
+    value_scale: float = 1.0
+    k0_boost: float = 1.0           # K at logical position 0 multiplied by this
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def rows(self) -> int:
+        return self.q_len * self.group
+
+    @property
+    def blocks_per_seq(self) -> int:
+        return self.capacity // self.block_size
+
+    def replace(self, **kw) -> "Case":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the decode-attention path, at full size.
+TINY = Case("tiny", seed=1, batch=1, num_q_heads=4, num_kv_heads=4, head_dim=64,
+            dtype="f32", cache_mode="contiguous", capacity=256, seq_lens=(256,),
+            value_scale=1.0)
+DECODE_7B = Case("decode_7b", seed=2, batch=16, num_q_heads=32, num_kv_heads=32,
+                 head_dim=128, dtype="f16", cache_mode="contiguous", capacity=4096,
+                 seq_len_range=(1024, 4096), value_scale=0.5)
+SPEC_VERIFY = Case("spec_verify", seed=3, batch=8, num_q_heads=64, num_kv_heads=8,
+                   head_dim=128, dtype="bf16", cache_mode="contiguous", capacity=8192,
+                   q_len=5, seq_lens=(8192,) * 8, value_scale=0.5)
+SINK_WINDOW = Case("sink_window", seed=4, batch=4, num_q_heads=32, num_kv_heads=32,
+                   head_dim=128, dtype="f16", cache_mode="ring", capacity=32768,
+                   mask_mode="sink_window", n_sink=4, window=4092,
+                   seq_lens=(32768, 36000, 100000, 1000000), value_scale=0.5,
+                   k0_boost=4.0)
+PAGED_100K = Case("paged_100k", seed=5, batch=2, num_q_heads=32, num_kv_heads=8,
+                  head_dim=128, dtype="bf16", cache_mode="paged", capacity=100000,
+                  block_size=16, num_blocks=12500, seq_lens=(100000, 100000),
+                  value_scale=0.5)
+
+CONFIGS = {c.name: c for c in (TINY, DECODE_7B, SPEC_VERIFY, SINK_WINDOW, PAGED_100K)}
+
+
+def cache_shape(case: Case) -> Tuple[int, ...]:
+    if case.cache_mode == "paged":
+        return (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
+    return (case.batch, case.capacity, case.num_kv_heads, case.head_dim)
+
+
+def make_inputs(case: Case, device: str = "cpu") -> dict:
+    """Draw one input set for `case`.
+
+    device="cpu" draws with torch's CPU generator (identical on every machine).
+    device="cuda" draws the same distributions with torch's device generator
+    seeded the same way (a different stream of values, made where the data
+    will live, which keeps multi-GiB caches fast to build).  The integer
+    structure is always drawn on the CPU generator so it is the same either way.
+    Returns a dict of tensors on `device` plus "case".
+    """
+    g_cpu = torch.Generator("cpu").manual_seed(case.seed)
+
+    # 1. integer structure
+    if case.seq_lens is not None:
+        assert len(case.seq_lens) == case.batch
+        seq_lens = torch.tensor(case.seq_lens, dtype=torch.int32)
+    else:
+        lo, hi = case.seq_len_range
+        seq_lens = torch.randint(lo, hi + 1, (case.batch,), generator=g_cpu,
+                                 dtype=torch.int64).to(torch.int32)
+    block_table = None
+    if case.cache_mode == "paged":
+        need = case.batch * case.blocks_per_seq
+        assert case.capacity % case.block_size == 0 and need <= case.num_blocks
+        perm = torch.randperm(case.num_blocks, generator=g_cpu)
+        block_table = perm[:need].view(case.batch, case.blocks_per_seq).to(torch.int32).contiguous()
+
+    # 2. values (float32 standard normals)
+    if device == "cpu":
+        g = g_cpu
+    else:
+        g = torch.Generator(device).manual_seed(case.seed)
+    qshape = (case.batch, case.q_len, case.num_q_heads, case.head_dim)
+    dt = DTYPES[case.dtype]
+    out = {}
+    for name, shape in (("q", qshape), ("k_cache", cache_shape(case)), ("v_cache", cache_shape(case))):
+        x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+        # 3. scale
+        if case.value_scale != 1.0:
+            x.mul_(case.value_scale)
+        if name == "k_cache" and case.k0_boost != 1.0:
+            # Logical position 0 of each sequence.  Contiguous and ring caches
+            # keep position 0 in the sequence's first slot (sink tokens are
+            # never evicted); a paged cache keeps it at offset 0 of the block
+            # the first page-table entry names.
+            if case.cache_mode == "paged":
+                for b in range(case.batch):
+                    x[int(block_table[b, 0]), 0].mul_(case.k0_boost)
+            else:
+                x[:, 0].mul_(case.k0_boost)
+        # 4. cast
+        out[name] = x.to(dt) if dt != torch.float32 else x
+        del x
+    out["seq_lens"] = seq_lens.to(device)
+    out["block_table"] = block_table.to(device) if block_table is not None else None
+    out["case"] = case
+    return out
+
+
+def small_variants():
+    """Reduced cases of each workload for element-by-element checks: several
+    tiles per split, ragged tails, the same structure as the full sizes."""
+    return {
+        "tiny": TINY,
+        "decode_7b_small": DECODE_7B.replace(name="decode_7b_small", batch=5, num_q_heads=4,
+                                             num_kv_heads=4, capacity=1200,
+                                             seq_len_range=(1, 1200), seed=12),
+        "spec_verify_small": SPEC_VERIFY.replace(name="spec_verify_small", batch=3,
+                                                 num_q_heads=16, num_kv_heads=2, capacity=1000,
+                                                 seq_lens=(1000, 517, 5), seed=13),
+        "sink_window_small": SINK_WINDOW.replace(name="sink_window_small", batch=4,
+                                                 num_q_heads=4, num_kv_heads=4, capacity=700,
+                                                 n_sink=4, window=300,
+                                                 seq_lens=(700, 1013, 5000, 250), seed=14),
+        "paged_small": PAGED_100K.replace(name="paged_small", batch=3, num_q_heads=8,
+                                          num_kv_heads=2, capacity=1600, num_blocks=310,
+                                          seq_lens=(1600, 1377, 33), seed=15),
+    }
