@@ -1,0 +1,172 @@
+/*
+ * kvattn - one decode step of attention over a KV cache, on AMD MI355X (gfx950).
+ *
+ * The operation (dothoosh.com StreamingLLM article, "The softmax problem"):
+ *
+ *     out = softmax(Q K^T / sqrt(d)) V
+ *
+ * for a block of q_len new query rows of each sequence against that sequence's
+ * cached keys and values ("KV cache" item of the nextadmin.net lesson "KV cache
+ * and Flash Attention": each new token is one query against the cached keys).
+ * q_len = 1 is plain autoregressive decode; q_len = 1 + k is the verification
+ * pass of speculative decoding, where every new row sees all earlier positions
+ * (dothoosh.com speculative-decoding article, "verify phase").
+ *
+ * Cache forms:
+ *   CONTIGUOUS  each sequence owns `capacity` consecutive slots; position p is slot p.
+ *   PAGED       16-token (block_size) blocks from a shared pool; a page table maps
+ *               logical page p / block_size to a physical block (lesson, "PagedAttention").
+ *   RING        StreamingLLM cache: the first n_sink positions keep slots 0..n_sink-1
+ *               for ever, later positions roll over the remaining capacity - n_sink
+ *               slots: slot = n_sink + (p - n_sink) mod (capacity - n_sink)
+ *               (StreamingLLM article, "The StreamingLLM solution").
+ *
+ * Masks:
+ *   KVATTN_MASK_CAUSAL       new row i of a sequence of T positions sits at
+ *                            P = T - q_len + i and sees every position p <= P.
+ *   KVATTN_MASK_SINK_WINDOW  row at P sees p <= P with p < n_sink (attention sinks)
+ *                            or p >= P - window + 1 (the `window` most recent
+ *                            positions, its own included).
+ *
+ * Layouts (row-major, head_dim innermost and contiguous; element type = dtype):
+ *   q, out       [batch, q_len, num_q_heads, head_dim]
+ *   CONTIGUOUS and RING caches
+ *                token-major (default): [batch, capacity, num_kv_heads, head_dim]
+ *                head-major:            [batch, num_kv_heads, capacity, head_dim]
+ *   PAGED cache  token-major (default): [num_blocks, block_size, num_kv_heads, head_dim]
+ *                head-major:            [num_blocks, num_kv_heads, block_size, head_dim]
+ *   block_table  int32 [batch, capacity / block_size]  (PAGED only)
+ *   seq_lens     int32 [batch]: T_b, every cached position of sequence b including
+ *                the q_len new ones, whose K and V are already in the cache.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped-query attention).
+ *
+ * Memory: every pointer passed to kvattn_decode is a device pointer owned by the
+ * caller and must stay valid until the work enqueued on the handle's stream has
+ * finished.  The handle owns one device workspace, allocated by kvattn_create;
+ * kvattn_decode never allocates, never synchronises and never copies to the host,
+ * so a call can be captured into a HIP graph.
+ *
+ * Errors: every entry point returns KVATTN_OK (0) or a negative code and never
+ * aborts; kvattn_last_error() gives the text of the calling thread's last error.
+ * Values that live on the device (seq_lens, block_table) are not checked on the
+ * host: the kernels clamp T to what the cache can hold (CONTIGUOUS/PAGED: T <=
+ * capacity) and skip page-table entries outside [0, num_blocks), so they never
+ * read outside the caller's buffers; a row with no attended position (T < q_len)
+ * gets zeros.
+ *
+ * Threads: one handle serves one stream; concurrent decode calls on one handle
+ * race on its workspace.  Use one handle per in-flight step.
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KVATTN_API __attribute__((visibility("default")))
+#else
+#define KVATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kvattn_status {
+    KVATTN_OK = 0,
+    KVATTN_ERR_INVALID_ARG = -1,   /* null pointer, bad enum, inconsistent sizes */
+    KVATTN_ERR_UNSUPPORTED = -2,   /* dtype / head_dim / mode combination not built */
+    KVATTN_ERR_CAPACITY = -3,      /* batch or q_len beyond what the handle was created for */
+    KVATTN_ERR_HIP = -4            /* a HIP runtime call failed (text in kvattn_last_error) */
+};
+
+enum kvattn_dtype { KVATTN_F32 = 0, KVATTN_F16 = 1, KVATTN_BF16 = 2 };
+enum kvattn_cache_mode { KVATTN_CONTIGUOUS = 0, KVATTN_PAGED = 1, KVATTN_RING = 2 };
+enum kvattn_mask_mode { KVATTN_MASK_CAUSAL = 0, KVATTN_MASK_SINK_WINDOW = 1 };
+enum kvattn_layout { KVATTN_LAYOUT_TOKEN_MAJOR = 0, KVATTN_LAYOUT_HEAD_MAJOR = 1 };
+
+typedef struct kvattn_config {
+    int32_t dtype;          /* kvattn_dtype: q, both caches and out share it */
+    int32_t num_q_heads;    /* Hq >= 1 */
+    int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
+    int32_t head_dim;       /* 64 or 128 */
+    int32_t max_batch;      /* >= 1 */
+    int32_t max_q_len;      /* 1 .. 64 */
+    int32_t cache_mode;     /* kvattn_cache_mode */
+    int32_t capacity;       /* CONTIGUOUS / RING: slots per sequence; PAGED: positions per
+                               sequence = block_size * (row length of block_table) */
+    int32_t block_size;     /* PAGED: power of two (16 in the lesson); otherwise ignored */
+    int32_t num_blocks;     /* PAGED: blocks in the pool; otherwise ignored */
+    int32_t layout;         /* kvattn_layout */
+    float scale;            /* 0 => 1 / sqrt(head_dim) */
+} kvattn_config;
+
+typedef struct kvattn_handle kvattn_handle;
+
+/* Validate `cfg`, plan the work decomposition and allocate the handle's device
+ * workspace (split partials) on the current HIP device.  *out is NULL on error. */
+KVATTN_API int kvattn_create(const kvattn_config* cfg, kvattn_handle** out);
+
+/*
+ * Enqueue one decode step on the handle's stream and return.
+ *   q            [batch, q_len, Hq, D]           device, read
+ *   k_cache      cache of keys (layout above)     device, read
+ *   v_cache      cache of values (same layout)    device, read
+ *   block_table  [batch, capacity / block_size]   device, read; PAGED only, else NULL
+ *   seq_lens     [batch] int32                    device, read
+ *   q_len        1 .. max_q_len
+ *   mask_mode    kvattn_mask_mode; RING requires KVATTN_MASK_SINK_WINDOW
+ *   n_sink       >= 0, window >= 1               (SINK_WINDOW only; ignored for CAUSAL)
+ *                RING: n_sink + window + q_len - 1 <= capacity and n_sink < capacity
+ *   out          [batch, q_len, Hq, D]           device, written
+ * batch is the handle's current batch (kvattn_set_batch; initially max_batch).
+ */
+KVATTN_API int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,
+                  int32_t mask_mode, int32_t n_sink, int32_t window, void* out);
+
+/* Free the workspace and the handle.  NULL is a no-op.  No enqueued decode may
+ * still be using the handle. */
+KVATTN_API void kvattn_destroy(kvattn_handle* h);
+
+/* Stream for later decode calls (a hipStream_t; NULL = the null stream). */
+KVATTN_API int kvattn_set_stream(kvattn_handle* h, void* stream);
+
+/* Batch for later decode calls, 0 .. max_batch (0 enqueues nothing). */
+KVATTN_API int kvattn_set_batch(kvattn_handle* h, int32_t batch);
+
+/* Force the number of attended positions per split-KV work item (a multiple of
+ * 64, or 0 to let the library choose).  For tests of split-count invariance. */
+KVATTN_API int kvattn_set_split_len(kvattn_handle* h, int32_t split_len);
+
+/* The decomposition a decode with these host arguments would use:
+ * n_split work items per (sequence, KV head) of split_len positions each, and
+ * the kernel family (0 = vector-ALU rows, 1 = matrix-core rows). */
+KVATTN_API int kvattn_plan(const kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
+                int32_t window, int32_t* n_split, int32_t* split_len, int32_t* kernel);
+
+/* Device bytes kvattn_create would allocate for `cfg`. */
+KVATTN_API int kvattn_workspace_bytes(const kvattn_config* cfg, size_t* bytes);
+
+/* Text of the calling thread's last error ("" if none). */
+KVATTN_API const char* kvattn_last_error(void);
+
+/*
+ * Test entry: for each (b, i) with b < batch, i < q_len, write the flat slot
+ * indices (rows of the [slots, Hkv, D] view of the cache; PAGED: block * block_size
+ * + offset) of every position row i of sequence b attends, in increasing
+ * position order, to slots_out[(b * q_len + i) * max_slots + j], and the count to
+ * counts_out[b * q_len + i] (counts beyond max_slots are still counted; only the
+ * first max_slots slots are written).  Uses the same device gather code as the
+ * decode kernels.  Device pointers; enqueued on the handle's stream.
+ */
+KVATTN_API int kvattn_debug_gather(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t q_len, int32_t mask_mode, int32_t n_sink, int32_t window,
+                        int32_t max_slots, int32_t* slots_out, int32_t* counts_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVATTN_H */

@@ -1,0 +1,236 @@
+"""Thin ctypes binding of libkvattn.so (include/kvattn.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the handle's stream, and every step of the computation runs in
+the library's HIP kernels.  There is no fallback: without the built library
+(or without a GPU) these calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvattn.so")
+
+KVATTN_OK = 0
+STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "HIP"}
+DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+CACHE = {"contiguous": 0, "paged": 1, "ring": 2}
+MASK = {"causal": 0, "sink_window": 1}
+LAYOUT = {"token_major": 0, "head_major": 1}
+
+EXPORTS = ("kvattn_create", "kvattn_decode", "kvattn_destroy", "kvattn_set_stream",
+           "kvattn_set_batch", "kvattn_set_split_len", "kvattn_plan", "kvattn_workspace_bytes",
+           "kvattn_last_error", "kvattn_debug_gather")
+
+
+class kvattn_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "dtype", "num_q_heads", "num_kv_heads", "head_dim", "max_batch", "max_q_len",
+        "cache_mode", "capacity", "block_size", "num_blocks", "layout")] + [
+        ("scale", ctypes.c_float)]
+
+
+class KVAttnError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libkvattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run kv_cache_attention_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+    H = ctypes.c_void_p
+    lib.kvattn_create.argtypes = [ctypes.POINTER(kvattn_config), ctypes.POINTER(H)]
+    lib.kvattn_create.restype = ctypes.c_int
+    lib.kvattn_decode.argtypes = [H, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.kvattn_decode.restype = ctypes.c_int
+    lib.kvattn_destroy.argtypes = [H]
+    lib.kvattn_destroy.restype = None
+    lib.kvattn_set_stream.argtypes = [H, vp]
+    lib.kvattn_set_stream.restype = ctypes.c_int
+    lib.kvattn_set_batch.argtypes = [H, i32]
+    lib.kvattn_set_batch.restype = ctypes.c_int
+    lib.kvattn_set_split_len.argtypes = [H, i32]
+    lib.kvattn_set_split_len.restype = ctypes.c_int
+    lib.kvattn_plan.argtypes = [H, i32, i32, i32, i32, i32p, i32p, i32p]
+    lib.kvattn_plan.restype = ctypes.c_int
+    lib.kvattn_workspace_bytes.argtypes = [ctypes.POINTER(kvattn_config),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvattn_workspace_bytes.restype = ctypes.c_int
+    lib.kvattn_last_error.argtypes = []
+    lib.kvattn_last_error.restype = ctypes.c_char_p
+    lib.kvattn_debug_gather.argtypes = [H, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.kvattn_debug_gather.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != KVATTN_OK:
+        raise KVAttnError(rc, where, load().kvattn_last_error().decode())
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def make_config(*, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                max_batch: int, max_q_len: int, cache_mode: str, capacity: int,
+                block_size: int = 16, num_blocks: int = 0, layout: str = "token_major",
+                scale: float = 0.0) -> kvattn_config:
+    return kvattn_config(DTYPE[dtype], num_q_heads, num_kv_heads, head_dim, max_batch, max_q_len,
+                         CACHE[cache_mode], capacity, block_size, num_blocks, LAYOUT[layout],
+                         scale)
+
+
+# ------------------------------------------------------------ same names as the C ABI
+
+def kvattn_create(cfg: kvattn_config) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load().kvattn_create(ctypes.byref(cfg), ctypes.byref(h)), "kvattn_create")
+    return h
+
+
+def kvattn_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len: int, mask_mode: int,
+                  n_sink: int, window: int, out) -> None:
+    _check(load().kvattn_decode(h, _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+                                _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_table, "block_table"),
+                                _dev_ptr(seq_lens, "seq_lens"), q_len, mask_mode, n_sink, window,
+                                _dev_ptr(out, "out")), "kvattn_decode")
+
+
+def kvattn_destroy(h) -> None:
+    load().kvattn_destroy(h)
+
+
+def kvattn_set_stream(h, stream: int) -> None:
+    _check(load().kvattn_set_stream(h, ctypes.c_void_p(stream)), "kvattn_set_stream")
+
+
+def kvattn_set_batch(h, batch: int) -> None:
+    _check(load().kvattn_set_batch(h, batch), "kvattn_set_batch")
+
+
+def kvattn_set_split_len(h, split_len: int) -> None:
+    _check(load().kvattn_set_split_len(h, split_len), "kvattn_set_split_len")
+
+
+def kvattn_plan(h, q_len: int, mask_mode: int, n_sink: int, window: int):
+    ns, sl, kern = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load().kvattn_plan(h, q_len, mask_mode, n_sink, window, ctypes.byref(ns),
+                              ctypes.byref(sl), ctypes.byref(kern)), "kvattn_plan")
+    return ns.value, sl.value, kern.value
+
+
+def kvattn_workspace_bytes(cfg: kvattn_config) -> int:
+    n = ctypes.c_size_t()
+    _check(load().kvattn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "kvattn_workspace_bytes")
+    return n.value
+
+
+def kvattn_last_error() -> str:
+    return load().kvattn_last_error().decode()
+
+
+def kvattn_debug_gather(h, block_table, seq_lens, q_len: int, mask_mode: int, n_sink: int,
+                        window: int, max_slots: int, slots_out, counts_out) -> None:
+    _check(load().kvattn_debug_gather(h, _dev_ptr(block_table, "block_table"),
+                                      _dev_ptr(seq_lens, "seq_lens"), q_len, mask_mode, n_sink,
+                                      window, max_slots, _dev_ptr(slots_out, "slots_out"),
+                                      _dev_ptr(counts_out, "counts_out")), "kvattn_debug_gather")
+
+
+# ------------------------------------------------------------ convenience wrapper
+
+class KVAttn:
+    """One handle: a fixed problem shape and its workspace on the current device."""
+
+    def __init__(self, *, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 max_batch: int, max_q_len: int, cache_mode: str, capacity: int,
+                 block_size: int = 16, num_blocks: int = 0, layout: str = "token_major",
+                 scale: float = 0.0):
+        self.cfg = make_config(dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                               head_dim=head_dim, max_batch=max_batch, max_q_len=max_q_len,
+                               cache_mode=cache_mode, capacity=capacity, block_size=block_size,
+                               num_blocks=num_blocks, layout=layout, scale=scale)
+        self.dtype = dtype
+        self.h = kvattn_create(self.cfg)
+
+    @classmethod
+    def for_case(cls, case, layout: str = "token_major", max_batch: Optional[int] = None,
+                 max_q_len: Optional[int] = None) -> "KVAttn":
+        return cls(dtype=case.dtype, num_q_heads=case.num_q_heads,
+                   num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                   max_batch=max_batch or case.batch, max_q_len=max_q_len or case.q_len,
+                   cache_mode=case.cache_mode, capacity=case.capacity,
+                   block_size=case.block_size, num_blocks=case.num_blocks, layout=layout)
+
+    def close(self) -> None:
+        if self.h:
+            kvattn_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_batch(self, batch: int) -> None:
+        kvattn_set_batch(self.h, batch)
+
+    def set_split_len(self, split_len: int) -> None:
+        kvattn_set_split_len(self.h, split_len)
+
+    def plan(self, q_len: int, mask_mode: str = "causal", n_sink: int = 0, window: int = 0):
+        return kvattn_plan(self.h, q_len, MASK[mask_mode], n_sink, window)
+
+    def decode(self, q, k_cache, v_cache, block_table, seq_lens, q_len: int,
+               mask_mode: str = "causal", n_sink: int = 0, window: int = 0, out=None,
+               stream: Optional[torch.cuda.Stream] = None):
+        want = TORCH_DTYPE[self.dtype]
+        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+            if t.dtype != want:
+                raise ValueError(f"{name} must be {want}")
+        if seq_lens.dtype != torch.int32 or (block_table is not None and
+                                              block_table.dtype != torch.int32):
+            raise ValueError("seq_lens and block_table must be int32")
+        if out is None:
+            out = torch.empty_like(q)
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        kvattn_set_stream(self.h, st.cuda_stream)
+        kvattn_decode(self.h, q, k_cache, v_cache, block_table, seq_lens, q_len, MASK[mask_mode],
+                      n_sink, window, out)
+        return out
+
+    def debug_gather(self, block_table, seq_lens, q_len: int, mask_mode: str = "causal",
+                     n_sink: int = 0, window: int = 0, max_slots: int = 0, batch: int = 1):
+        dev = seq_lens.device
+        slots = torch.full((batch * q_len * max(max_slots, 1),), -2, dtype=torch.int32, device=dev)
+        counts = torch.zeros(batch * q_len, dtype=torch.int32, device=dev)
+        kvattn_set_stream(self.h, torch.cuda.current_stream(dev).cuda_stream)
+        kvattn_debug_gather(self.h, block_table, seq_lens, q_len, MASK[mask_mode], n_sink, window,
+                            max_slots, slots, counts)
+        return slots.view(batch, q_len, max(max_slots, 1)), counts.view(batch, q_len)

@@ -1,0 +1,370 @@
+// Split-KV flash-decoding on the vector ALUs, for up to 16 query rows per KV head.
+//
+// One workgroup (256 lanes = 4 wave64) owns one (sequence, KV head, split): a
+// run of split_len attended positions.  Each position's K row (and V row) of
+// head_dim elements is read by one "lane group" of head_dim*bytes/16 lanes with
+// one 16-byte load per lane, so a wave instruction covers whole 256-byte rows and
+// every byte of K and V is loaded exactly once, straight into registers (each
+// byte feeds exactly one lane, so staging it through LDS would add a write and a
+// read with no reuse).  All query rows that share the KV head (the GQA group
+// times the q_len new tokens) live in every lane, so one K/V fetch serves the
+// whole group.
+//
+// Per tile of U positions a lane group forms the scores with packed dot
+// products, sums them over its lanes with DPP, and folds them into its own
+// running (max, sum, accumulator) - the online softmax of the Flash Attention
+// section of the nextadmin.net lesson "KV cache and Flash Attention" (running
+// max and sum across tiles, rescale the old terms by exp(m_old - m_new), which
+// is 0 when nothing was seen yet).  Scores are kept in the exp2 domain
+// (scale * log2 e folded into one multiply).  At the end the lane groups of a
+// wave merge through cross-lane shuffles, the four waves through LDS, and the
+// workgroup writes either the final row (one split) or its unnormalised
+// partial (acc, m, l) for the log-sum-exp merge kernel.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace kvattn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT, int D>
+struct Geo {
+    static constexpr int EB = Elem<DT>::bytes;
+    static constexpr int EPL = 16 / EB;   // elements per lane (one 16-byte load)
+    static constexpr int LPR = D / EPL;   // lanes per (position, head) row
+};
+
+constexpr int VALU_THREADS = 256;
+
+__device__ __forceinline__ u32x4 load16(const void* base, int64_t elem_off, int eb) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + elem_off * eb);
+}
+
+// q . k over one lane's 16 bytes
+template <int DT>
+__device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b) {
+    float s = 0.0f;
+    if constexpr (DT == F16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a[e]),
+                                       __builtin_bit_cast(half2_t, b[e]), s, false);
+    } else if constexpr (DT == BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2_t, a[e]),
+                                                __builtin_bit_cast(short2_t, b[e]), s, false);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(__uint_as_float(a[e]), __uint_as_float(b[e]), s);
+    }
+    return s;
+}
+
+// one lane's 16 bytes as EPL floats
+template <int DT>
+__device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (DT == F16) {
+            f[2 * e] = f16_lo(w[e]);
+            f[2 * e + 1] = f16_hi(w[e]);
+        } else if constexpr (DT == BF16) {
+            f[2 * e] = bf16_lo(w[e]);
+            f[2 * e + 1] = bf16_hi(w[e]);
+        } else {
+            f[e] = __uint_as_float(w[e]);
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
+    if constexpr (DT == F32)
+        reinterpret_cast<float*>(out)[idx] = x;
+    else if constexpr (DT == F16)
+        reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_bits(x);
+    else
+        reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(x);
+}
+
+template <int DT, int D, int ROWS, int CACHE, int U>
+__global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeParams p,
+                                                                   int row_blocks) {
+    using G = Geo<DT, D>;
+    constexpr int EPL = G::EPL, LPR = G::LPR, EB = G::EB;
+    constexpr int NLG = VALU_THREADS / LPR;  // lane groups per workgroup
+    constexpr float NEG_INF = -__builtin_inff();
+
+    const int split = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z / row_blocks;
+    const int rb = blockIdx.z - b * row_blocks;
+
+    const SeqSpan s = seq_span(p, b);
+    if (split >= valid_splits(p, s)) return;
+    const int32_t j0 = split * p.split_len;
+    const int32_t j1 = min(j0 + p.split_len, s.count);
+
+    const int tid = threadIdx.x;
+    const int lane = tid % LPR;
+    const int lg = tid / LPR;
+    const int d0 = lane * EPL;
+
+    // Query rows of this KV head: row r = i * group + hg  (new token i, head kvh*group+hg)
+    u32x4 qv[ROWS];
+    int row_i[ROWS];
+    int64_t row_id[ROWS];  // index of the row in out's [batch, q_len, Hq] order
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const int rg = rb * ROWS + r;
+        const bool ok = rg < p.rows;
+        const int i = ok ? rg / p.group : 0;
+        const int h = kvh * p.group + (ok ? rg - i * p.group : 0);
+        row_i[r] = ok ? i : -1;
+        row_id[r] = ((int64_t)b * p.q_len + i) * p.num_q_heads + h;
+        qv[r] = ok ? load16(p.q, row_id[r] * D + d0, EB) : u32x4{0, 0, 0, 0};
+    }
+
+    float m[ROWS], l[ROWS], acc[ROWS][EPL];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        m[r] = NEG_INF;
+        l[r] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[r][e] = 0.0f;
+    }
+    // With one new row per sequence the attended union is exactly that row's set.
+    const bool per_row_mask = p.q_len > 1;
+
+    for (int32_t base = j0; base < j1; base += NLG * U) {
+        u32x4 kw[U], vw[U];
+        int32_t pos[U];
+        bool val[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = base + u * NLG + lg;
+            val[u] = j < j1;
+            pos[u] = 0;
+            int64_t off = 0;
+            if (val[u]) {
+                pos[u] = span_pos(s, j);
+                const Loc L = locate<CACHE>(p, s, b, pos[u]);
+                val[u] = L.unit >= 0;
+                off = row_offset(p, L, kvh) + d0;
+            }
+            // positions outside the attended set are never loaded: they may hold
+            // anything (NaN included) and must not reach the accumulator
+            kw[u] = val[u] ? load16(p.k, off, EB) : u32x4{0, 0, 0, 0};
+            vw[u] = val[u] ? load16(p.v, off, EB) : u32x4{0, 0, 0, 0};
+        }
+        float sc[ROWS][U];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float x = group_sum<LPR>(dot16<DT>(qv[r], kw[u])) * p.scale_log2;
+                bool ok = val[u];
+                if (per_row_mask) ok = ok && row_i[r] >= 0 && row_attends(p, s, row_i[r], pos[u]);
+                sc[r][u] = ok ? x : NEG_INF;
+            }
+        }
+        float vf[U][EPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) unpack16<DT>(vw[u], vf[u]);
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            float mt = sc[r][0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[r][u]);
+            const float m_new = fmaxf(m[r], mt);
+            const float m_use = m_new == NEG_INF ? 0.0f : m_new;
+            const float alpha = fast_exp2(m[r] - m_use);  // 0 while nothing was seen
+            l[r] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[r][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float pw = fast_exp2(sc[r][u] - m_use);
+                l[r] += pw;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(pw, vf[u][e], acc[r][e]);
+            }
+            m[r] = m_new;
+        }
+    }
+
+    // Merge the lane groups of each wave (butterfly over lane offsets LPR .. 32).
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const float mo = __shfl_xor(m[r], off, 64);
+            const float lo = __shfl_xor(l[r], off, 64);
+            const float M = fmaxf(m[r], mo);
+            const float Mu = M == NEG_INF ? 0.0f : M;
+            const float a = fast_exp2(m[r] - Mu);
+            const float c = fast_exp2(mo - Mu);
+            l[r] = l[r] * a + lo * c;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float ao = __shfl_xor(acc[r][e], off, 64);
+                acc[r][e] = acc[r][e] * a + ao * c;
+            }
+            m[r] = M;
+        }
+    }
+
+    // Merge the four waves through LDS.
+    constexpr int NW = VALU_THREADS / 64;
+    __shared__ float sm_acc[NW][ROWS][D];
+    __shared__ float sm_ml[NW][ROWS][2];
+    const int wave = tid / 64;
+    const int lw = tid % 64;
+    if (lw < LPR) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_acc[wave][r][d0 + e] = acc[r][e];
+            if (lw == 0) {
+                sm_ml[wave][r][0] = m[r];
+                sm_ml[wave][r][1] = l[r];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < ROWS * D; idx += VALU_THREADS) {
+        const int r = idx / D;
+        const int d = idx - r * D;
+        if (rb * ROWS + r >= p.rows) continue;
+        float M = NEG_INF;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][r][0]);
+        const float Mu = M == NEG_INF ? 0.0f : M;
+        float L = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = fast_exp2(sm_ml[w][r][0] - Mu);
+            L += sm_ml[w][r][1] * f;
+            A += sm_acc[w][r][d] * f;
+        }
+        // recompute this row's id (registers indexed by a runtime r are avoided)
+        const int rg = rb * ROWS + r;
+        const int i = rg / p.group;
+        const int h = kvh * p.group + (rg - i * p.group);
+        const int64_t rid = ((int64_t)b * p.q_len + i) * p.num_q_heads + h;
+        if (p.n_split == 1) {
+            store_out<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
+        } else {
+            const int64_t part = rid * p.n_split + split;
+            p.ws_acc[part * D + d] = A;
+            if (d == 0) {
+                p.ws_ml[part * 2] = M;
+                p.ws_ml[part * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// Log-sum-exp merge of the split partials: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+template <int DT, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p, int64_t rows_total) {
+    constexpr int RPB = 256 / D;  // rows per block
+    const int64_t rid = (int64_t)blockIdx.x * RPB + threadIdx.x / D;
+    const int d = threadIdx.x % D;
+    if (rid >= rows_total) return;
+    const int b = (int)(rid / ((int64_t)p.q_len * p.num_q_heads));
+    const SeqSpan s = seq_span(p, b);
+    const int nv = valid_splits(p, s);
+    const float* ml = p.ws_ml + rid * p.n_split * 2;
+    const float* acc = p.ws_acc + rid * p.n_split * D;
+    float M = -__builtin_inff();
+    for (int sp = 0; sp < nv; ++sp) M = fmaxf(M, ml[sp * 2]);
+    const float Mu = M == -__builtin_inff() ? 0.0f : M;
+    float L = 0.0f, A = 0.0f;
+    for (int sp = 0; sp < nv; ++sp) {
+        const float f = fast_exp2(ml[sp * 2] - Mu);
+        L += ml[sp * 2 + 1] * f;
+        A += acc[(int64_t)sp * D + d] * f;
+    }
+    store_out<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
+}
+
+// ---------------------------------------------------------------- host launchers
+
+template <int DT, int D, int ROWS, int CACHE>
+static hipError_t launch_valu_t(const DecodeParams& p, int row_blocks, hipStream_t st) {
+    constexpr int U = ROWS >= 8 ? 4 : 8;  // positions per lane group per tile
+    dim3 grid(p.n_split, p.num_kv_heads, p.batch * row_blocks);
+    hipLaunchKernelGGL((decode_valu_kernel<DT, D, ROWS, CACHE, U>), grid, dim3(VALU_THREADS), 0,
+                       st, p, row_blocks);
+    return hipGetLastError();
+}
+
+template <int DT, int D, int ROWS>
+static hipError_t launch_valu_c(const DecodeParams& p, int row_blocks, hipStream_t st) {
+    switch (p.cache_mode) {
+    case CONTIGUOUS: return launch_valu_t<DT, D, ROWS, CONTIGUOUS>(p, row_blocks, st);
+    case PAGED: return launch_valu_t<DT, D, ROWS, PAGED>(p, row_blocks, st);
+    default: return launch_valu_t<DT, D, ROWS, RING>(p, row_blocks, st);
+    }
+}
+
+template <int DT, int D>
+static hipError_t launch_valu_r(const DecodeParams& p, int rows_per_block, int row_blocks,
+                                hipStream_t st) {
+    switch (rows_per_block) {
+    case 1: return launch_valu_c<DT, D, 1>(p, row_blocks, st);
+    case 2: return launch_valu_c<DT, D, 2>(p, row_blocks, st);
+    case 4: return launch_valu_c<DT, D, 4>(p, row_blocks, st);
+    case 8: return launch_valu_c<DT, D, 8>(p, row_blocks, st);
+    default: return launch_valu_c<DT, D, 16>(p, row_blocks, st);
+    }
+}
+
+int valu_rows_per_block(int rows) {
+    if (rows <= 1) return 1;
+    if (rows <= 2) return 2;
+    if (rows <= 4) return 4;
+    if (rows <= 8) return 8;
+    return 16;
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
+    const int rpb = valu_rows_per_block(p.rows);
+    const int row_blocks = (p.rows + rpb - 1) / rpb;
+    if (head_dim == 128) {
+        switch (dtype) {
+        case F16: return launch_valu_r<F16, 128>(p, rpb, row_blocks, st);
+        case BF16: return launch_valu_r<BF16, 128>(p, rpb, row_blocks, st);
+        default: return launch_valu_r<F32, 128>(p, rpb, row_blocks, st);
+        }
+    }
+    switch (dtype) {
+    case F16: return launch_valu_r<F16, 64>(p, rpb, row_blocks, st);
+    case BF16: return launch_valu_r<BF16, 64>(p, rpb, row_blocks, st);
+    default: return launch_valu_r<F32, 64>(p, rpb, row_blocks, st);
+    }
+}
+
+hipError_t launch_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
+    const int64_t rows_total = (int64_t)p.batch * p.q_len * p.num_q_heads;
+    const int rpb = 256 / head_dim;
+    const dim3 grid((unsigned)((rows_total + rpb - 1) / rpb));
+    if (head_dim == 128) {
+        switch (dtype) {
+        case F16: hipLaunchKernelGGL((merge_kernel<F16, 128>), grid, dim3(256), 0, st, p, rows_total); break;
+        case BF16: hipLaunchKernelGGL((merge_kernel<BF16, 128>), grid, dim3(256), 0, st, p, rows_total); break;
+        default: hipLaunchKernelGGL((merge_kernel<F32, 128>), grid, dim3(256), 0, st, p, rows_total); break;
+        }
+    } else {
+        switch (dtype) {
+        case F16: hipLaunchKernelGGL((merge_kernel<F16, 64>), grid, dim3(256), 0, st, p, rows_total); break;
+        case BF16: hipLaunchKernelGGL((merge_kernel<BF16, 64>), grid, dim3(256), 0, st, p, rows_total); break;
+        default: hipLaunchKernelGGL((merge_kernel<F32, 64>), grid, dim3(256), 0, st, p, rows_total); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvattn

@@ -1,0 +1,204 @@
+// Device-side building blocks shared by every kernel of the library: the
+// per-launch parameter block, the attended-set and gather arithmetic (the one
+// definition of which cache slot holds which position), element conversions
+// and wavefront reductions.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvattn {
+
+enum : int { F32 = 0, F16 = 1, BF16 = 2 };
+enum : int { CONTIGUOUS = 0, PAGED = 1, RING = 2 };
+enum : int { MASK_CAUSAL = 0, MASK_SINK_WINDOW = 1 };
+
+// Everything a decode launch needs, passed by value as the kernel argument.
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* out;
+    float* ws_acc;        // [rows_total, n_split, D]  split partials (unnormalised)
+    float* ws_ml;         // [rows_total, n_split, 2]  (running max m, sum l), log2 domain
+    int64_t stride_seq;   // elements: sequence (contiguous/ring) or block (paged)
+    int64_t stride_head;  // elements: KV head
+    int64_t stride_tok;   // elements: slot within a sequence / block
+    int32_t batch, num_q_heads, num_kv_heads, group, q_len, rows;
+    int32_t cache_mode, mask_mode, n_sink, window;
+    int32_t capacity, log2_block, num_blocks, blocks_per_seq;
+    int32_t n_split, split_len;
+    float scale_log2;     // softmax scale * log2(e): scores are kept in the exp2 domain
+};
+
+// The attended positions of one sequence, over all q_len new rows, are the union
+// [0, sink) + [tail, T): sink positions (attention sinks) and one trailing run.
+// Work is indexed by j in [0, count): j < sink -> position j, else tail + (j - sink).
+struct SeqSpan {
+    int32_t T;      // clamped length
+    int32_t sink;   // attended sink positions
+    int32_t tail;   // first position of the trailing run
+    int32_t count;  // attended positions in the union
+    int32_t ring_pos0;  // RING: first attended position at or past n_sink ...
+    int32_t ring0;      // ... and its offset within the rolling slots
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const DecodeParams& p, int b) {
+    SeqSpan s;
+    int32_t T = p.seq_lens[b];
+    if (T < 0) T = 0;
+    // Contiguous and paged caches cannot hold more than `capacity` positions.
+    if (p.cache_mode != RING && T > p.capacity) T = p.capacity;
+    s.T = T;
+    s.sink = 0;
+    s.tail = 0;
+    if (p.mask_mode == MASK_SINK_WINDOW) {
+        const int32_t sk = min(p.n_sink, T);
+        // first position any row's window reaches: row 0 sits at T - q_len
+        const int64_t w0 = max<int64_t>((int64_t)T - p.q_len - p.window + 1, 0);
+        if (w0 > sk) {
+            s.sink = sk;
+            s.tail = (int32_t)w0;
+        }
+    }
+    s.count = s.sink + (T - s.tail);
+    // Ring slots: positions past the sinks roll over R = capacity - n_sink slots.  The
+    // attended ones past the sinks are consecutive and span at most R positions, so
+    // their slots follow from one modulo at the first of them.
+    s.ring_pos0 = max(s.tail, p.n_sink);
+    s.ring0 = 0;
+    if (p.cache_mode == RING && p.n_sink < p.capacity)
+        s.ring0 = (s.ring_pos0 - p.n_sink) % (p.capacity - p.n_sink);
+    return s;
+}
+
+// Logical position of work index j.
+__device__ __forceinline__ int32_t span_pos(const SeqSpan& s, int32_t j) {
+    return j < s.sink ? j : s.tail + (j - s.sink);
+}
+
+// Where position `pos` of sequence b lives: `unit` is the sequence (contiguous,
+// ring) or the pool block (paged) and `idx` the slot inside it.  unit < 0 when the
+// page table names a block outside the pool (the position is then skipped).
+struct Loc {
+    int64_t unit;
+    int32_t idx;
+};
+
+template <int CACHE>
+__device__ __forceinline__ Loc locate(const DecodeParams& p, const SeqSpan& s, int b,
+                                      int32_t pos) {
+    Loc l;
+    if constexpr (CACHE == CONTIGUOUS) {
+        (void)s;
+        l.unit = b;
+        l.idx = pos;
+    } else if constexpr (CACHE == RING) {
+        l.unit = b;
+        if (pos < p.n_sink) {
+            l.idx = pos;  // sinks are never evicted
+        } else {
+            const int32_t R = p.capacity - p.n_sink;
+            int32_t r = s.ring0 + (pos - s.ring_pos0);
+            if (r >= R) r -= R;
+            l.idx = p.n_sink + r;
+        }
+    } else {
+        (void)s;
+        const int32_t blk = p.block_table[(int64_t)b * p.blocks_per_seq + (pos >> p.log2_block)];
+        l.unit = (uint32_t)blk < (uint32_t)p.num_blocks ? (int64_t)blk : -1;
+        l.idx = pos & ((1 << p.log2_block) - 1);
+    }
+    return l;
+}
+
+// Element offset of the (location, KV head) row of a cache.
+__device__ __forceinline__ int64_t row_offset(const DecodeParams& p, const Loc& l, int kvh) {
+    return l.unit * p.stride_seq + (int64_t)kvh * p.stride_head + (int64_t)l.idx * p.stride_tok;
+}
+
+// Flat slot index, independent of the layout: b * capacity + slot, or
+// block * block_size + offset.
+template <int CACHE>
+__device__ __forceinline__ int64_t flat_slot(const DecodeParams& p, const Loc& l) {
+    if (l.unit < 0) return -1;
+    if constexpr (CACHE == PAGED)
+        return (l.unit << p.log2_block) + l.idx;
+    else
+        return l.unit * p.capacity + l.idx;
+}
+
+// Does new row i (query position T - q_len + i) attend position pos?
+__device__ __forceinline__ bool row_attends(const DecodeParams& p, const SeqSpan& s, int i,
+                                            int32_t pos) {
+    const int32_t P = s.T - p.q_len + i;
+    if (pos > P) return false;
+    if (p.mask_mode == MASK_CAUSAL) return true;
+    return pos < p.n_sink || pos >= P - p.window + 1;
+}
+
+// Number of split work items that hold attended positions for a sequence (>= 1:
+// split 0 always runs so that an empty sequence still produces its zero rows).
+__device__ __forceinline__ int32_t valid_splits(const DecodeParams& p, const SeqSpan& s) {
+    const int32_t n = (s.count + p.split_len - 1) / p.split_len;
+    return n < 1 ? 1 : (n > p.n_split ? p.n_split : n);
+}
+
+// ---------------------------------------------------------------- element types
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+
+template <int DT> struct Elem;
+template <> struct Elem<F32> { static constexpr int bytes = 4; };
+template <> struct Elem<F16> { static constexpr int bytes = 2; };
+template <> struct Elem<BF16> { static constexpr int bytes = 2; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Round-to-nearest-even stores.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// ---------------------------------------------------------------- cross-lane sums
+
+// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of the group
+// receives the same value.  Steps pair lanes with commutative adds, so all lanes
+// hold bit-identical results.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16 || N == 32, "group size");
+    // quad_perm [1,0,3,2]: swap neighbours
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, false);
+    // quad_perm [2,3,0,1]: swap pairs
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, false);
+    // row_half_mirror: lane i <-> 7 - i within each 8
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, false);
+    if constexpr (N >= 16) {
+        // row_mirror: lane i <-> 15 - i within each 16
+        x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, false);
+    }
+    if constexpr (N == 32) {
+        x += __shfl_xor(x, 16, 64);
+    }
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace kvattn

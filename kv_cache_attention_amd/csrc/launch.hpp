@@ -1,0 +1,25 @@
+// Host-side launchers of the device kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+
+namespace kvattn {
+
+// Vector-ALU split-KV kernel (any row count; rows above 16 run in blocks of 16).
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
+int valu_rows_per_block(int rows);
+
+// Matrix-core split-KV kernel for 16 or more rows per KV head (f16 / bf16).
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
+bool mfma_supported(int dtype, int head_dim, int rows);
+
+// Log-sum-exp merge of split partials into `out`.
+hipError_t launch_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
+
+// Test entry: the slots each new row attends, through the kernels' own gather code.
+hipError_t launch_debug_gather(const DecodeParams& p, int max_slots, int32_t* slots_out,
+                               int32_t* counts_out, hipStream_t st);
+
+}  // namespace kvattn

@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by element.
+
+Reduced-size versions of every workload (several tiles per split, ragged tails),
+never-attended slots poisoned with NaN, both cache layouts, forced split counts,
+sharp (far from uniform) softmax variants, the q = 0 closed form, page-table
+permutations, and the degenerate lengths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_attention_amd import binding as kb
+from kv_cache_attention_amd import workloads
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+SMALL = workloads.small_variants()
+
+
+def _prep(case, scale_q=1.0):
+    inp = workloads.make_inputs(case)
+    if scale_q != 1.0:
+        inp["q"] = (inp["q"].float() * scale_q).to(inp["q"].dtype)
+    gh.poison_unattended(case, inp)
+    ref = oracle.decode(case, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
+                        inp["seq_lens"])
+    return inp, ref
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("layout", ["token_major", "head_major"])
+def test_small_workloads_match_oracle(name, layout):
+    case = SMALL[name]
+    print(f"case={name} layout={layout}", flush=True)
+    inp, ref = _prep(case)
+    out = gh.run(case, gh.to_device(inp), layout=layout)
+    gh.check(out, ref, case.dtype, f"{name}/{layout}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_sharp_softmax_matches_oracle(name):
+    """q x 8: weights far from uniform, so a dropped split or a wrong rescale shows."""
+    case = SMALL[name]
+    print(f"case={name} sharp", flush=True)
+    inp, ref = _prep(case, scale_q=8.0)
+    out = gh.run(case, gh.to_device(inp))
+    gh.check(out, ref, case.dtype, f"{name}/sharp")
+
+
+@pytest.mark.parametrize("name", ["decode_7b_small", "spec_verify_small", "sink_window_small",
+                                  "paged_small"])
+@pytest.mark.parametrize("split_len", [64, 128, 192, 512])
+def test_split_count_does_not_change_the_result(name, split_len):
+    case = SMALL[name]
+    print(f"case={name} split_len={split_len}", flush=True)
+    inp, ref = _prep(case, scale_q=4.0)
+    out = gh.run(case, gh.to_device(inp), split_len=split_len)
+    gh.check(out, ref, case.dtype, f"{name}/split{split_len}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_q_zero_gives_mean_of_attended_values(name):
+    """Equal scores -> uniform weights: each row is the mean of V over its attended set."""
+    case = SMALL[name]
+    print(f"case={name} q=0", flush=True)
+    inp = workloads.make_inputs(case)
+    gh.poison_unattended(case, inp)
+    inp["q"].zero_()
+    vflat = inp["v_cache"].reshape(-1, case.num_kv_heads, case.head_dim).double()
+    ref = np.zeros((case.batch, case.q_len, case.num_q_heads, case.head_dim))
+    for b in range(case.batch):
+        for i in range(case.q_len):
+            _, slots = oracle.attended(case, inp["block_table"], inp["seq_lens"], b, i)
+            if len(slots) == 0:
+                continue
+            mean = vflat[torch.as_tensor(slots)].mean(0).numpy()  # [Hkv, D]
+            ref[b, i] = np.repeat(mean, case.group, axis=0)
+    out = gh.run(case, gh.to_device(inp))
+    gh.check(out, ref, case.dtype, f"{name}/q0")
+
+
+def test_page_permutation_is_bit_identical():
+    """The same logical sequences under two different page tables give the same bits."""
+    case = SMALL["paged_small"]
+    inp = workloads.make_inputs(case)
+    bt1 = inp["block_table"]
+    perm = torch.randperm(case.num_blocks, generator=torch.Generator().manual_seed(99))
+    # move every physical block p to perm[p]; the table follows it
+    bt2 = perm[bt1.long()].int()
+    k2 = torch.empty_like(inp["k_cache"])
+    v2 = torch.empty_like(inp["v_cache"])
+    k2[perm] = inp["k_cache"]
+    v2[perm] = inp["v_cache"]
+    d1 = gh.to_device(inp)
+    d2 = dict(d1, block_table=bt2.cuda(), k_cache=k2.cuda(), v_cache=v2.cuda())
+    o1 = gh.run(case, d1)
+    o2 = gh.run(case, d2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["sink_window_small", "paged_small", "decode_7b_small",
+                                  "spec_verify_small"])
+def test_gather_indices_are_bit_exact(name):
+    """kvattn_debug_gather (the kernels' own gather code) lists exactly the oracle's slots."""
+    case = SMALL[name]
+    inp = workloads.make_inputs(case)
+    d = gh.to_device(inp)
+    h = kb.KVAttn.for_case(case)
+    max_slots = case.capacity
+    slots, counts = h.debug_gather(d["block_table"], d["seq_lens"], case.q_len, case.mask_mode,
+                                   case.n_sink, case.window, max_slots, batch=case.batch)
+    slots, counts = slots.cpu().numpy(), counts.cpu().numpy()
+    for b in range(case.batch):
+        for i in range(case.q_len):
+            _, ref = oracle.attended(case, inp["block_table"], inp["seq_lens"], b, i)
+            assert counts[b, i] == len(ref), (b, i)
+            assert np.array_equal(slots[b, i, :len(ref)], ref), (b, i)
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 300, 303, 304, 305, 700, 701, 1003, 5000])
+@pytest.mark.parametrize("q_len", [1, 5])
+def test_ring_gather_edges(T, q_len):
+    """Ring edge lengths: T in {1, n_sink, n_sink+1, n_sink+window(+ql-1), S, S+1, wraps}."""
+    case = SINK = SMALL["sink_window_small"].replace(batch=1, seq_lens=(T,), q_len=q_len,
+                                                     num_q_heads=4, num_kv_heads=4)
+    sl = torch.tensor([T], dtype=torch.int32)
+    h = kb.KVAttn.for_case(SINK)
+    slots, counts = h.debug_gather(None, sl.cuda(), q_len, case.mask_mode, case.n_sink,
+                                   case.window, case.capacity, batch=1)
+    slots, counts = slots.cpu().numpy(), counts.cpu().numpy()
+    for i in range(q_len):
+        _, ref = oracle.attended(case, None, sl, 0, i)
+        assert counts[0, i] == len(ref)
+        assert np.array_equal(slots[0, i, :len(ref)], ref)
+
+
+def test_degenerate_lengths():
+    """T = 0 gives zero rows; T < q_len gives zero rows for the rows with no position;
+    T = 1 returns V of the one position."""
+    case = workloads.Case("deg", seed=31, batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                          dtype="f16", cache_mode="contiguous", capacity=256, q_len=3,
+                          seq_lens=(0, 1, 2, 256), value_scale=0.5)
+    inp, ref = _prep(case)
+    out = gh.run(case, gh.to_device(inp))
+    gh.check(out, ref, case.dtype, "degenerate")
+    o = out.float().cpu()
+    assert torch.all(o[0] == 0)
+    assert torch.all(o[1, :2] == 0) and torch.all(o[2, :1] == 0)
+
+
+def test_batch_zero_and_subset_batches():
+    case = SMALL["decode_7b_small"]
+    inp, ref = _prep(case)
+    d = gh.to_device(inp)
+    h = kb.KVAttn.for_case(case)
+    out = torch.full_like(d["q"], 7.0)
+    h.set_batch(0)
+    h.decode(d["q"], d["k_cache"], d["v_cache"], None, d["seq_lens"], 1, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    h.set_batch(2)
+    h.decode(d["q"], d["k_cache"], d["v_cache"], None, d["seq_lens"], 1, out=out)
+    torch.cuda.synchronize()
+    gh.check(out[:2], ref[:2], case.dtype, "batch2")
+    assert torch.all(out[2:] == 7.0)
+
+
+def test_lengths_beyond_capacity_are_clamped():
+    """A device-side length past the cache's end is clamped, never read past the buffer."""
+    case = SMALL["decode_7b_small"].replace(seq_len_range=None, seq_lens=(1200,) * 5)
+    inp, ref = _prep(case)
+    d = gh.to_device(inp)
+    d["seq_lens"] = torch.full((5,), 1_000_000, dtype=torch.int32, device="cuda")
+    out = gh.run(case, d)
+    gh.check(out, ref, case.dtype, "clamped")
+
+
+def test_host_side_errors_with_a_device():
+    case = SMALL["sink_window_small"]
+    inp = gh.to_device(workloads.make_inputs(case))
+    h = kb.KVAttn.for_case(case)
+    with pytest.raises(kb.KVAttnError) as e:   # window too large for the ring
+        h.decode(inp["q"], inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 1,
+                 "sink_window", 4, case.capacity)
+    assert e.value.code == -1
+    with pytest.raises(kb.KVAttnError) as e:   # ring needs the sink/window mask
+        h.decode(inp["q"], inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 1, "causal")
+    assert e.value.code == -1
+    with pytest.raises(kb.KVAttnError) as e:   # q_len beyond the handle
+        h.decode(inp["q"], inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 2,
+                 "sink_window", 4, 300)
+    assert e.value.code == -3
+    with pytest.raises(kb.KVAttnError) as e:
+        h.set_batch(case.batch + 1)
+    assert e.value.code == -3
