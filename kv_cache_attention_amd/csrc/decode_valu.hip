@@ -44,16 +44,22 @@ __device__ __forceinline__ u32x4 load16(const void* base, int64_t elem_off, int 
 template <int DT>
 __device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b) {
     float s = 0.0f;
+    // (each vector element goes through a scalar first: bit-casting a vector
+    // element expression directly is miscompiled to element 0 by this toolchain)
     if constexpr (DT == F16) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a[e]),
-                                       __builtin_bit_cast(half2_t, b[e]), s, false);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t x = a[e], y = b[e];
+            s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x),
+                                       __builtin_bit_cast(half2_t, y), s, false);
+        }
     } else if constexpr (DT == BF16) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2_t, a[e]),
-                                                __builtin_bit_cast(short2_t, b[e]), s, false);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t x = a[e], y = b[e];
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(short2_t, x),
+                                                __builtin_bit_cast(short2_t, y), s, false);
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) s = fmaf(__uint_as_float(a[e]), __uint_as_float(b[e]), s);

@@ -18,6 +18,7 @@ def _sample_rows(case, n=40, seed=0):
     rng = np.random.default_rng(seed)
     rows = {(b, case.q_len - 1, h) for b in range(case.batch) for h in (0, case.num_q_heads - 1)}
     rows |= {(b, 0, 0) for b in range(case.batch)}
+    n = min(n, case.batch * case.q_len * case.num_q_heads)
     while len(rows) < n:
         rows.add((int(rng.integers(case.batch)), int(rng.integers(case.q_len)),
                   int(rng.integers(case.num_q_heads))))
