@@ -22,10 +22,13 @@ int fail(int code, const std::string& msg) {
     return code;
 }
 
-// Split-KV decomposition targets about 8 workgroups per compute unit
-// (256 CUs), with at least 256 attended positions per split.
+// Split-KV decomposition: about 8 workgroups per compute unit (256 CUs) for the
+// vector-ALU kernel, with at least 256 attended positions per split; the
+// matrix-core kernel holds one or two workgroups per CU and wants longer splits.
 constexpr int kTargetWorkgroups = 2048;
 constexpr int kMinSplitLen = 256;
+constexpr int kTargetWorkgroupsMfma = 512;
+constexpr int kMinSplitLenMfma = 512;
 constexpr int kSplitQuantum = 64;
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxQLen = 64;
@@ -83,9 +86,10 @@ int row_blocks_of(const kvattn_config& c, int q_len) {
 // Automatic split count for `batch` sequences of up to n_att attended positions.
 void auto_plan(const kvattn_config& c, int batch, int q_len, int64_t n_att, int* n_split,
                int* split_len) {
+    const bool mfma = use_mfma(c, q_len);
     const int64_t units = (int64_t)(batch > 0 ? batch : 1) * c.num_kv_heads * row_blocks_of(c, q_len);
-    int ns = ceil_div(kTargetWorkgroups, units);
-    const int ns_cap = ceil_div(n_att > 0 ? n_att : 1, kMinSplitLen);
+    int ns = ceil_div(mfma ? kTargetWorkgroupsMfma : kTargetWorkgroups, units);
+    const int ns_cap = ceil_div(n_att > 0 ? n_att : 1, mfma ? kMinSplitLenMfma : kMinSplitLen);
     if (ns > ns_cap) ns = ns_cap;
     if (ns < 1) ns = 1;
     if (ns > kMaxSplits) ns = kMaxSplits;
