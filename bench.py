@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark one decode step of attention over a KV cache on one MI355X.
 
-A step is one kvattn_decode call over one batch of the workload: every split-KV
-workgroup plus the log-sum-exp merge, the whole batch, one layer.  Inputs are
+A step is one kvattn_decode call over one batch of the workload: one kernel
+launch (every split-KV workgroup, with the log-sum-exp merge done by the last
+workgroup of each sequence and KV head), the whole batch, one layer.  Inputs are
 seeded synthetic tensors already resident in HBM.  Several identical copies of
 the K/V caches are rotated between steps so that each step streams its K/V from
 HBM rather than from the 256 MB last-level (Infinity) cache.
@@ -95,7 +96,7 @@ def main():
     kv_attended = step_bytes - 2 * case.batch * case.q_len * case.num_q_heads * case.head_dim * \
         accounting.ELEM_BYTES[case.dtype]
 
-    copies = a.copies or max(2, -(-4 * MALL_BYTES // max(kv_attended, 1)))
+    copies = a.copies or min(64, max(2, -(-4 * MALL_BYTES // max(kv_attended, 1))))
     kcs, vcs = [d["k_cache"]], [d["v_cache"]]
     for _ in range(copies - 1):
         kcs.append(d["k_cache"].clone())
@@ -179,7 +180,8 @@ def main():
             "flops_per_step": step_flops,
             "event_us_mean": round(ev_mean * 1e3, 2),
             "event_us_median": round(ev_med * 1e3, 2),
-            "timed": "decode kernel + merge kernel per step (HIP events on the library stream)",
+            "timed": "the decode kernel (split-KV + fused merge), one launch per step, "
+                     "HIP events on the library's stream",
         },
     }
     if not a.no_cpu_baseline:

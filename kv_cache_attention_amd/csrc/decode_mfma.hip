@@ -24,10 +24,13 @@
 // row for each 16-position half; two halves give the 8 positions of the P^T
 // operand, and V^T is read back with the same position permutation.
 // The next tile's K and V are loaded before the current tile's math: K into a
-// second register buffer, V into the one V buffer just emptied into LDS.  The four waves then merge through LDS and
-// the workgroup writes the final rows (one split) or its partial (acc, m, l).
+// second register buffer, V into the one V buffer just emptied into LDS.  The
+// four waves then merge through LDS and the workgroup writes the final rows (its
+// sequence needs one split) or its partial (acc, m, l); the last workgroup of the
+// (sequence, KV head) merges the partials (split_merge.hpp).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "split_merge.hpp"
 
 namespace kvattn {
 
@@ -59,14 +62,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
         return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
-template <int DT>
-__device__ __forceinline__ void store_out_m(void* out, int64_t idx, float x) {
-    if constexpr (DT == F16)
-        reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_bits(x);
-    else
-        reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(x);
-}
-
 template <int D>
 struct MfmaGeo {
     static constexpr int KS = D / 32;                // k-steps of 32 along d
@@ -94,7 +89,8 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
     const SeqSpan s = seq_span(p, b);
-    if (split >= valid_splits(p, s)) return;
+    const int nvalid = valid_splits(p, s);
+    if (split >= nvalid) return;
     const int32_t j0 = split * p.split_len;
     const int32_t j1 = min(j0 + p.split_len, s.count);
 
@@ -345,19 +341,25 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
 #pragma unroll
         for (int w = 0; w < MFMA_WAVES; ++w) L += sm_l[w][n] * fast_exp2(sm_m[w][n] - Mu);
         const float A = osum[idx];
-        const int i = n / p.group;
-        const int h = kvh * p.group + (n - i * p.group);
-        const int64_t rid = ((int64_t)b * p.q_len + i) * p.num_q_heads + h;
-        if (p.n_split == 1) {
-            store_out_m<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
+        const int64_t rid = row_id_of(p, b, kvh, n);
+        if (nvalid == 1) {
+            store_elem<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
         } else {
             const int64_t part = rid * p.n_split + split;
-            p.ws_acc[part * D + d] = A;
+            store_partial(p.ws_acc + part * D + d, A);
             if (d == 0) {
-                p.ws_ml[part * 2] = M;
-                p.ws_ml[part * 2 + 1] = L;
+                store_partial(p.ws_ml + part * 2, M);
+                store_partial(p.ws_ml + part * 2 + 1, L);
             }
         }
+    }
+    if (nvalid > 1) {
+        // the staging area is free again: the merge's scratch lives there
+        static_assert(sizeof(MergeSmem<NQ, MFMA_THREADS>) <= SMEM_V, "merge scratch");
+        __syncthreads();
+        auto& msm = *reinterpret_cast<MergeSmem<NQ, MFMA_THREADS>*>(smem);
+        arrive_and_merge<DT, D, NQ, MFMA_THREADS>(p, b, kvh, 0, b * p.num_kv_heads + kvh, nvalid,
+                                                  msm);
     }
 }
 

@@ -18,10 +18,15 @@
 // is 0 when nothing was seen yet).  Scores are kept in the exp2 domain
 // (scale * log2 e folded into one multiply).  At the end the lane groups of a
 // wave merge through cross-lane shuffles, the four waves through LDS, and the
-// workgroup writes either the final row (one split) or its unnormalised
-// partial (acc, m, l) for the log-sum-exp merge kernel.
+// workgroup writes either the final rows (its sequence needs one split) or its
+// unnormalised partial (acc, m, l); the last workgroup of the (sequence, KV
+// head) to finish merges the partials (split_merge.hpp).
+//
+// Paged caches: the page-table entries of the next tile are read while the
+// current tile is processed, so the K/V loads never wait on a table read.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "split_merge.hpp"
 
 namespace kvattn {
 
@@ -84,16 +89,6 @@ __device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
     }
 }
 
-template <int DT>
-__device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
-    if constexpr (DT == F32)
-        reinterpret_cast<float*>(out)[idx] = x;
-    else if constexpr (DT == F16)
-        reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_bits(x);
-    else
-        reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(x);
-}
-
 template <int DT, int D, int ROWS, int CACHE, int U>
 __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeParams p,
                                                                    int row_blocks) {
@@ -108,7 +103,8 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
     const int rb = blockIdx.z - b * row_blocks;
 
     const SeqSpan s = seq_span(p, b);
-    if (split >= valid_splits(p, s)) return;
+    const int nvalid = valid_splits(p, s);
+    if (split >= nvalid) return;
     const int32_t j0 = split * p.split_len;
     const int32_t j1 = min(j0 + p.split_len, s.count);
 
@@ -143,6 +139,16 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
     // With one new row per sequence the attended union is exactly that row's set.
     const bool per_row_mask = p.q_len > 1;
 
+    // page-table entries of the current tile (paged caches), read one tile ahead
+    int32_t blk[U];
+    if constexpr (CACHE == PAGED) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = j0 + u * NLG + lg;
+            blk[u] = j < j1 ? page_entry(p, b, span_pos(s, j)) : -1;
+        }
+    }
+
     for (int32_t base = j0; base < j1; base += NLG * U) {
         u32x4 kw[U], vw[U];
         int32_t pos[U];
@@ -155,7 +161,11 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
             int64_t off = 0;
             if (val[u]) {
                 pos[u] = span_pos(s, j);
-                const Loc L = locate<CACHE>(p, s, b, pos[u]);
+                Loc L;
+                if constexpr (CACHE == PAGED)
+                    L = paged_loc(p, blk[u], pos[u]);
+                else
+                    L = locate<CACHE>(p, s, b, pos[u]);
                 val[u] = L.unit >= 0;
                 off = row_offset(p, L, kvh) + d0;
             }
@@ -163,6 +173,13 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
             // anything (NaN included) and must not reach the accumulator
             kw[u] = val[u] ? load16(p.k, off, EB) : u32x4{0, 0, 0, 0};
             vw[u] = val[u] ? load16(p.v, off, EB) : u32x4{0, 0, 0, 0};
+        }
+        if constexpr (CACHE == PAGED) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t j = base + NLG * U + u * NLG + lg;
+                blk[u] = j < j1 ? page_entry(p, b, span_pos(s, j)) : -1;
+            }
         }
         float sc[ROWS][U];
 #pragma unroll
@@ -254,46 +271,23 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
             L += sm_ml[w][r][1] * f;
             A += sm_acc[w][r][d] * f;
         }
-        // recompute this row's id (registers indexed by a runtime r are avoided)
-        const int rg = rb * ROWS + r;
-        const int i = rg / p.group;
-        const int h = kvh * p.group + (rg - i * p.group);
-        const int64_t rid = ((int64_t)b * p.q_len + i) * p.num_q_heads + h;
-        if (p.n_split == 1) {
-            store_out<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
+        const int64_t rid = row_id_of(p, b, kvh, rb * ROWS + r);
+        if (nvalid == 1) {
+            store_elem<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
         } else {
             const int64_t part = rid * p.n_split + split;
-            p.ws_acc[part * D + d] = A;
+            store_partial(p.ws_acc + part * D + d, A);
             if (d == 0) {
-                p.ws_ml[part * 2] = M;
-                p.ws_ml[part * 2 + 1] = L;
+                store_partial(p.ws_ml + part * 2, M);
+                store_partial(p.ws_ml + part * 2 + 1, L);
             }
         }
     }
-}
-
-// Log-sum-exp merge of the split partials: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-template <int DT, int D>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p, int64_t rows_total) {
-    constexpr int RPB = 256 / D;  // rows per block
-    const int64_t rid = (int64_t)blockIdx.x * RPB + threadIdx.x / D;
-    const int d = threadIdx.x % D;
-    if (rid >= rows_total) return;
-    const int b = (int)(rid / ((int64_t)p.q_len * p.num_q_heads));
-    const SeqSpan s = seq_span(p, b);
-    const int nv = valid_splits(p, s);
-    const float* ml = p.ws_ml + rid * p.n_split * 2;
-    const float* acc = p.ws_acc + rid * p.n_split * D;
-    float M = -__builtin_inff();
-    for (int sp = 0; sp < nv; ++sp) M = fmaxf(M, ml[sp * 2]);
-    const float Mu = M == -__builtin_inff() ? 0.0f : M;
-    float L = 0.0f, A = 0.0f;
-    for (int sp = 0; sp < nv; ++sp) {
-        const float f = fast_exp2(ml[sp * 2] - Mu);
-        L += ml[sp * 2 + 1] * f;
-        A += acc[(int64_t)sp * D + d] * f;
+    if (nvalid > 1) {
+        __shared__ MergeSmem<ROWS, VALU_THREADS> msm;
+        const int unit = (b * p.num_kv_heads + kvh) * row_blocks + rb;
+        arrive_and_merge<DT, D, ROWS, VALU_THREADS>(p, b, kvh, rb * ROWS, unit, nvalid, msm);
     }
-    store_out<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
 }
 
 // ---------------------------------------------------------------- host launchers
@@ -351,26 +345,6 @@ hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hi
     case BF16: return launch_valu_r<BF16, 64>(p, rpb, row_blocks, st);
     default: return launch_valu_r<F32, 64>(p, rpb, row_blocks, st);
     }
-}
-
-hipError_t launch_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
-    const int64_t rows_total = (int64_t)p.batch * p.q_len * p.num_q_heads;
-    const int rpb = 256 / head_dim;
-    const dim3 grid((unsigned)((rows_total + rpb - 1) / rpb));
-    if (head_dim == 128) {
-        switch (dtype) {
-        case F16: hipLaunchKernelGGL((merge_kernel<F16, 128>), grid, dim3(256), 0, st, p, rows_total); break;
-        case BF16: hipLaunchKernelGGL((merge_kernel<BF16, 128>), grid, dim3(256), 0, st, p, rows_total); break;
-        default: hipLaunchKernelGGL((merge_kernel<F32, 128>), grid, dim3(256), 0, st, p, rows_total); break;
-        }
-    } else {
-        switch (dtype) {
-        case F16: hipLaunchKernelGGL((merge_kernel<F16, 64>), grid, dim3(256), 0, st, p, rows_total); break;
-        case BF16: hipLaunchKernelGGL((merge_kernel<BF16, 64>), grid, dim3(256), 0, st, p, rows_total); break;
-        default: hipLaunchKernelGGL((merge_kernel<F32, 64>), grid, dim3(256), 0, st, p, rows_total); break;
-        }
-    }
-    return hipGetLastError();
 }
 
 }  // namespace kvattn

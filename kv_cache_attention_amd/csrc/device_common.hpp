@@ -23,6 +23,7 @@ struct DecodeParams {
     void* out;
     float* ws_acc;        // [rows_total, n_split, D]  split partials (unnormalised)
     float* ws_ml;         // [rows_total, n_split, 2]  (running max m, sum l), log2 domain
+    int32_t* counters;    // [batch, Hkv, row blocks] arrivals per unit, 0 between calls
     int64_t stride_seq;   // elements: sequence (contiguous/ring) or block (paged)
     int64_t stride_head;  // elements: KV head
     int64_t stride_tok;   // elements: slot within a sequence / block
@@ -111,6 +112,18 @@ __device__ __forceinline__ Loc locate(const DecodeParams& p, const SeqSpan& s, i
         l.unit = (uint32_t)blk < (uint32_t)p.num_blocks ? (int64_t)blk : -1;
         l.idx = pos & ((1 << p.log2_block) - 1);
     }
+    return l;
+}
+
+// Paged caches in two steps, so the page-table read can be issued ahead of use:
+// the table entry of position pos, then the location it gives.
+__device__ __forceinline__ int32_t page_entry(const DecodeParams& p, int b, int32_t pos) {
+    return p.block_table[(int64_t)b * p.blocks_per_seq + (pos >> p.log2_block)];
+}
+__device__ __forceinline__ Loc paged_loc(const DecodeParams& p, int32_t blk, int32_t pos) {
+    Loc l;
+    l.unit = (uint32_t)blk < (uint32_t)p.num_blocks ? (int64_t)blk : -1;
+    l.idx = pos & ((1 << p.log2_block) - 1);
     return l;
 }
 

@@ -1,6 +1,7 @@
 // C-ABI host side of kvattn: argument validation, work decomposition, the
-// handle's workspace, and the launches on the caller's stream.  No call here
-// synchronises; kvattn_decode allocates nothing.
+// handle's workspace, and the launches on the caller's stream.  kvattn_create
+// allocates and clears the workspace (and waits for the clear); kvattn_decode
+// allocates nothing and never synchronises: one kernel launch per call.
 #include "../../include/kvattn.h"
 
 #include <hip/hip_runtime.h>
@@ -51,8 +52,9 @@ struct kvattn_handle {
     hipStream_t stream;
     int32_t batch;
     int32_t forced_split_len;
-    float* ws;              // split partials: acc [ws_rows, D] then (m, l) [ws_rows, 2]
+    float* ws;              // split partials: acc [ws_rows, D], (m, l) [ws_rows, 2], counters
     int64_t ws_rows;        // partial rows the workspace holds
+    int64_t n_units;        // arrival counters (batch x KV heads x row blocks)
     int64_t stride_seq, stride_head, stride_tok;
 };
 
@@ -114,6 +116,17 @@ int64_t workspace_rows(const kvattn_config& c) {
     const int64_t floor_splits = std::min<int64_t>(64, ceil_div(c.capacity, kSplitQuantum));
     const int64_t fl = (int64_t)c.max_batch * c.max_q_len * c.num_q_heads * floor_splits;
     return best > fl ? best : fl;
+}
+
+// Arrival counters: one per (sequence, KV head, block of 16 rows).
+int64_t counter_units(const kvattn_config& c) {
+    const int64_t rows = (int64_t)c.max_q_len * (c.num_q_heads / c.num_kv_heads);
+    return (int64_t)c.max_batch * c.num_kv_heads * ((rows + 15) / 16);
+}
+
+size_t workspace_size(const kvattn_config& c, int64_t ws_rows) {
+    return (size_t)ws_rows * (size_t)(c.head_dim + 2) * sizeof(float) +
+           (size_t)counter_units(c) * sizeof(int32_t);
 }
 
 int validate_config(const kvattn_config* c) {
@@ -202,7 +215,7 @@ int kvattn_workspace_bytes(const kvattn_config* cfg, size_t* bytes) {
     int rc = validate_config(cfg);
     if (rc) return rc;
     if (!bytes) return fail(KVATTN_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = (size_t)workspace_rows(*cfg) * (size_t)(cfg->head_dim + 2) * sizeof(float);
+    *bytes = workspace_size(*cfg, workspace_rows(*cfg));
     return KVATTN_OK;
 }
 
@@ -233,11 +246,20 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
         return fail(KVATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     }
     h->ws_rows = workspace_rows(*cfg);
-    const size_t bytes = (size_t)h->ws_rows * (size_t)(cfg->head_dim + 2) * sizeof(float);
+    h->n_units = counter_units(*cfg);
+    const size_t bytes = workspace_size(*cfg, h->ws_rows);
     e = hipMalloc(reinterpret_cast<void**>(&h->ws), bytes);
     if (e != hipSuccess) {
         delete h;
         return fail(KVATTN_ERR_HIP, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
+    }
+    // the arrival counters start at zero; every decode leaves them at zero
+    e = hipMemset(h->ws, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(h->ws);
+        delete h;
+        return fail(KVATTN_ERR_HIP, std::string("hipMemset(workspace): ") + hipGetErrorString(e));
     }
     *out = h;
     return KVATTN_OK;
@@ -298,6 +320,7 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.out = out;
     p.ws_acc = h->ws;
     p.ws_ml = h->ws + h->ws_rows * c.head_dim;
+    p.counters = reinterpret_cast<int32_t*>(h->ws + h->ws_rows * (c.head_dim + 2));
     p.stride_seq = h->stride_seq;
     p.stride_head = h->stride_head;
     p.stride_tok = h->stride_tok;
@@ -345,11 +368,6 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
                        : kvattn::launch_decode_valu(p, h->cfg.dtype, h->cfg.head_dim, h->stream);
     if (e != hipSuccess)
         return fail(KVATTN_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
-    if (ns > 1) {
-        e = kvattn::launch_merge(p, h->cfg.dtype, h->cfg.head_dim, h->stream);
-        if (e != hipSuccess)
-            return fail(KVATTN_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
-    }
     return KVATTN_OK;
 }
 

