@@ -89,7 +89,10 @@ __device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
     }
 }
 
-template <int DT, int D, int ROWS, int CACHE, int U>
+// MASKED: q_len > 1, so rows of one sequence attend different position sets and
+// every score gets its row's causal / window test (with one new row the attended
+// union is exactly that row's set and no per-row test is needed).
+template <int DT, int D, int ROWS, int CACHE, int U, bool MASKED>
 __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeParams p,
                                                                    int row_blocks) {
     using G = Geo<DT, D>;
@@ -136,20 +139,32 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[r][e] = 0.0f;
     }
-    // With one new row per sequence the attended union is exactly that row's set.
-    const bool per_row_mask = p.q_len > 1;
-
-    // page-table entries of the current tile (paged caches), read one tile ahead
-    int32_t blk[U];
-    if constexpr (CACHE == PAGED) {
+    // per-row bounds for MASKED: row r attends pos iff pos <= hi[r] and
+    // (pos < n_sink or pos >= lo[r])  (lo = 0 for the causal mask)
+    int32_t hi[ROWS], lo[ROWS];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t j = j0 + u * NLG + lg;
-            blk[u] = j < j1 ? page_entry(p, b, span_pos(s, j)) : -1;
-        }
+    for (int r = 0; r < ROWS; ++r) {
+        const int32_t P = s.T - p.q_len + (row_i[r] >= 0 ? row_i[r] : p.q_len - 1);
+        hi[r] = P;
+        lo[r] = p.mask_mode == MASK_SINK_WINDOW ? P - p.window + 1 : 0;
     }
 
-    for (int32_t base = j0; base < j1; base += NLG * U) {
+    // Loads are branch-free: a lane whose position lies past the split (or behind a
+    // page-table entry outside the pool) loads a clamped, valid address and its
+    // data is discarded by selects (score -> -inf, V -> 0), never multiplied in.
+    // Paged caches read the page-table entries one tile ahead of use.
+    constexpr int32_t TW = NLG * U;  // positions per workgroup tile
+    int32_t blk[U];
+    auto pages = [&](int32_t base) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = min(base + u * NLG + lg, j1 - 1);
+            blk[u] = page_entry(p, b, span_pos(s, j));
+        }
+    };
+    if constexpr (CACHE == PAGED) pages(j0);
+
+    for (int32_t base = j0; base < j1; base += TW) {
         u32x4 kw[U], vw[U];
         int32_t pos[U];
         bool val[U];
@@ -157,58 +172,62 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
         for (int u = 0; u < U; ++u) {
             const int32_t j = base + u * NLG + lg;
             val[u] = j < j1;
-            pos[u] = 0;
-            int64_t off = 0;
-            if (val[u]) {
-                pos[u] = span_pos(s, j);
-                Loc L;
-                if constexpr (CACHE == PAGED)
-                    L = paged_loc(p, blk[u], pos[u]);
-                else
-                    L = locate<CACHE>(p, s, b, pos[u]);
-                val[u] = L.unit >= 0;
-                off = row_offset(p, L, kvh) + d0;
+            pos[u] = span_pos(s, min(j, j1 - 1));
+            Loc L;
+            if constexpr (CACHE == PAGED) {
+                L = paged_loc(p, blk[u], pos[u]);
+                val[u] = val[u] && L.unit >= 0;
+                L.unit = L.unit >= 0 ? L.unit : 0;
+            } else {
+                L = locate<CACHE>(p, s, b, pos[u]);
             }
-            // positions outside the attended set are never loaded: they may hold
-            // anything (NaN included) and must not reach the accumulator
-            kw[u] = val[u] ? load16(p.k, off, EB) : u32x4{0, 0, 0, 0};
-            vw[u] = val[u] ? load16(p.v, off, EB) : u32x4{0, 0, 0, 0};
+            const int64_t off = row_offset(p, L, kvh) + d0;
+            kw[u] = load16(p.k, off, EB);
+            vw[u] = load16(p.v, off, EB);
         }
-        if constexpr (CACHE == PAGED) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t j = base + NLG * U + u * NLG + lg;
-                blk[u] = j < j1 ? page_entry(p, b, span_pos(s, j)) : -1;
-            }
-        }
+        if constexpr (CACHE == PAGED) pages(base + TW);
+        // raw scores q.k; the softmax scale (times log2 e) is applied inside the
+        // exp2 argument, so the running max m is kept in scaled units
         float sc[ROWS][U];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float x = group_sum<LPR>(dot16<DT>(qv[r], kw[u])) * p.scale_log2;
+                const float x = group_sum<LPR>(dot16<DT>(qv[r], kw[u]));
                 bool ok = val[u];
-                if (per_row_mask) ok = ok && row_i[r] >= 0 && row_attends(p, s, row_i[r], pos[u]);
+                if constexpr (MASKED)
+                    ok = ok & (pos[u] <= hi[r]) & ((pos[u] < p.n_sink) | (pos[u] >= lo[r]));
                 sc[r][u] = ok ? x : NEG_INF;
             }
         }
         float vf[U][EPL];
 #pragma unroll
-        for (int u = 0; u < U; ++u) unpack16<DT>(vw[u], vf[u]);
+        for (int u = 0; u < U; ++u) {
+            unpack16<DT>(vw[u], vf[u]);
+            // a paged position behind an out-of-pool entry was read from block 0 and
+            // may hold anything; every other discarded lane read an attended position
+            if constexpr (CACHE == PAGED) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) vf[u][e] = val[u] ? vf[u][e] : 0.0f;
+            }
+        }
+        const float c = p.scale_log2;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
             float mt = sc[r][0];
 #pragma unroll
             for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[r][u]);
-            const float m_new = fmaxf(m[r], mt);
+            const float m_new = fmaxf(m[r], mt * c);  // c > 0: max commutes with the scale
             const float m_use = m_new == NEG_INF ? 0.0f : m_new;
-            const float alpha = fast_exp2(m[r] - m_use);  // 0 while nothing was seen
-            l[r] *= alpha;
+            if (__any(m_new != m[r])) {  // rescale only when some lane's max moved
+                const float alpha = fast_exp2(m[r] - m_use);  // 0 while nothing was seen
+                l[r] *= alpha;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[r][e] *= alpha;
+                for (int e = 0; e < EPL; ++e) acc[r][e] *= alpha;
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const float pw = fast_exp2(sc[r][u] - m_use);
+                const float pw = fast_exp2(fmaf(sc[r][u], c, -m_use));
                 l[r] += pw;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(pw, vf[u][e], acc[r][e]);
@@ -292,12 +311,28 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
 
 // ---------------------------------------------------------------- host launchers
 
+// Positions per lane group per tile.
+#ifndef KVATTN_VALU_U_SMALL
+#define KVATTN_VALU_U_SMALL 8   // 1 or 2 rows
+#endif
+#ifndef KVATTN_VALU_U_MID
+#define KVATTN_VALU_U_MID 8     // 4 rows
+#endif
+#ifndef KVATTN_VALU_U_LARGE
+#define KVATTN_VALU_U_LARGE 4   // 8 or 16 rows
+#endif
+
 template <int DT, int D, int ROWS, int CACHE>
 static hipError_t launch_valu_t(const DecodeParams& p, int row_blocks, hipStream_t st) {
-    constexpr int U = ROWS >= 8 ? 4 : 8;  // positions per lane group per tile
+    constexpr int U = ROWS <= 2 ? KVATTN_VALU_U_SMALL
+                                : (ROWS <= 4 ? KVATTN_VALU_U_MID : KVATTN_VALU_U_LARGE);
     dim3 grid(p.n_split, p.num_kv_heads, p.batch * row_blocks);
-    hipLaunchKernelGGL((decode_valu_kernel<DT, D, ROWS, CACHE, U>), grid, dim3(VALU_THREADS), 0,
-                       st, p, row_blocks);
+    if (p.q_len > 1)
+        hipLaunchKernelGGL((decode_valu_kernel<DT, D, ROWS, CACHE, U, true>), grid,
+                           dim3(VALU_THREADS), 0, st, p, row_blocks);
+    else
+        hipLaunchKernelGGL((decode_valu_kernel<DT, D, ROWS, CACHE, U, false>), grid,
+                           dim3(VALU_THREADS), 0, st, p, row_blocks);
     return hipGetLastError();
 }
 
