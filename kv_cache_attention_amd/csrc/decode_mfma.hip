@@ -8,14 +8,14 @@
 // run as v_mfma_f32_16x16x32_{bf16,f16} tiles with fp32 accumulation.
 //
 // One workgroup (4 wave64) owns a (sequence, KV head, split); each wave takes
-// every 4th tile of 32 positions.  Per tile and wave:
-//   S^T[32 x rows] = K[32 x d] . Q^T[d x rows]   K straight from HBM into the
+// every 4th tile of 64 positions (32 for 49-64 rows).  Per tile and wave:
+//   S^T[64 x rows] = K[64 x d] . Q^T[d x rows]   K straight from HBM into the
 //                     A operand (each lane's 16 bytes are 8 consecutive d of one
 //                     position: the operand layout), Q^T held in registers;
 //   online softmax per row over the tile (running max / sum, as in the Flash
 //                     Attention section of the nextadmin.net lesson "KV cache
 //                     and Flash Attention"), P rounded to the input type;
-//   O^T[d x rows]  += V^T[d x 32] . P^T[32 x rows]   V needs positions along each
+//   O^T[d x rows]  += V^T[d x 64] . P^T[64 x rows]   V needs positions along each
 //                     lane's 8 operand elements while HBM holds it d-contiguous,
 //                     so V goes HBM -> registers -> LDS and is read back
 //                     transposed (2-byte reads from a padded, bank-conflict-free
@@ -23,8 +23,8 @@
 // The S^T accumulator already holds, per lane, 4 consecutive positions of one
 // row for each 16-position half; two halves give the 8 positions of the P^T
 // operand, and V^T is read back with the same position permutation.
-// The next tile's K and V are loaded before the current tile's math: K into a
-// second register buffer, V into the one V buffer just emptied into LDS.  The
+// The next tile's V is loaded as soon as this tile's V sits in LDS, its K as soon
+// as S^T has consumed this tile's K, so both are in flight during the rest.  The
 // four waves then merge through LDS and the workgroup writes the final rows (its
 // sequence needs one split) or its partial (acc, m, l); the last workgroup of the
 // (sequence, KV head) merges the partials (split_merge.hpp).
@@ -41,7 +41,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int MFMA_THREADS = 256;
 constexpr int MFMA_WAVES = MFMA_THREADS / 64;
-constexpr int TILE = 32;  // positions per wave step
+// Positions per wave step: 64 (32 when four row tiles leave too few registers).
+template <int R>
+struct MfmaTile {
+    static constexpr int TILE = R <= 3 ? 64 : 32;
+    static constexpr int TT = TILE / 16;  // 16-position sub-tiles (S^T accumulators)
+    static constexpr int KK = TILE / 32;  // 32-position k-steps of P V
+};
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -53,16 +59,35 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// two fp32 -> one dword of two 16-bit values (round to nearest even)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> one dword of two 16-bit values (v_cvt_pk_*: round to nearest even)
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
     if constexpr (DT == F16)
-        return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
     else
-        return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int D>
+// max / sum with the lanes 16 and 32 away (gfx950 permlane swaps, no LDS round trip)
+__device__ __forceinline__ float xmax_16_32(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float xsum_16_32(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+template <int D, int TILE>
 struct MfmaGeo {
     static constexpr int KS = D / 32;                // k-steps of 32 along d
     static constexpr int DT16 = D / 16;              // 16-wide d tiles of the output
@@ -72,7 +97,8 @@ struct MfmaGeo {
 
 template <int DT, int D, int R, int CACHE>
 __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeParams p) {
-    using G = MfmaGeo<D>;
+    constexpr int TILE = MfmaTile<R>::TILE, TT = MfmaTile<R>::TT, KK = MfmaTile<R>::KK;
+    using G = MfmaGeo<D, TILE>;
     constexpr int KS = G::KS, DT16 = G::DT16, VROW = G::VROW;
     constexpr float NEG_INF = -__builtin_inff();
     constexpr int NQ = R * 16;  // padded rows
@@ -141,59 +167,89 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
     const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k);
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v);
 
-    // K and V of one tile, in the A-operand lane mapping:
-    // position tile + tt*16 + lr, d chunk (ks*4 + lq)*8.
-    auto load_tile = [&](int32_t tb, u32x4 (&kf)[2][KS], u32x4 (&vf)[2][KS]) {
+    // K and V of one tile, in the A-operand lane mapping: position tile + tt*16 + lr,
+    // d chunk (ks*4 + lq)*8.  Loads are branch-free: a position past the split is
+    // clamped to the split's last one (an attended, finite row) and its scores are
+    // masked; a paged position behind an out-of-pool entry reads block 0 and both
+    // its score and its V are discarded by selects.
+    bool pvalid[TT];
+    int64_t offs[TT];
+    auto locate_tile = [&](int32_t tb) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int32_t j = tb + tt * 16 + lr;
-            bool val = j < j1;
-            int64_t off = 0;
-            if (val) {
-                const Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
-                val = L.unit >= 0;
-                off = row_offset(p, L, kvh);
-            }
-            // positions past the split or behind an invalid page entry are not
-            // loaded (they may hold NaN) and enter as zeros
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int64_t e = off + (ks * 4 + lq) * 8;
-                kf[tt][ks] = val ? *reinterpret_cast<const u32x4*>(kp + e) : u32x4{0, 0, 0, 0};
-                vf[tt][ks] = val ? *reinterpret_cast<const u32x4*>(vp + e) : u32x4{0, 0, 0, 0};
-            }
+        for (int tt = 0; tt < TT; ++tt) {
+            const int32_t j = min(tb + tt * 16 + lr, j1 - 1);
+            Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
+            pvalid[tt] = L.unit >= 0;
+            L.unit = L.unit >= 0 ? L.unit : 0;
+            offs[tt] = row_offset(p, L, kvh);
         }
+    };
+    auto load_k = [&](u32x4 (&kf)[TT][KS]) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[tt][ks] = *reinterpret_cast<const u32x4*>(kp + offs[tt] + (ks * 4 + lq) * 8);
+    };
+    auto load_v = [&](u32x4 (&vf)[TT][KS]) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                vf[tt][ks] = *reinterpret_cast<const u32x4*>(vp + offs[tt] + (ks * 4 + lq) * 8);
     };
 
     const int32_t step = MFMA_WAVES * TILE;
     int32_t tb = j0 + wave * TILE;
-    // K is double-buffered in registers; V has one register buffer, emptied into
-    // LDS before the next tile's V is loaded into it.
-    u32x4 kc[2][KS], kn[2][KS], vr[2][KS];
-    if (tb < j1) load_tile(tb, kc, vr);
+    // One register buffer each for K and V.  The next tile's V is loaded as soon as
+    // this tile's V is in LDS, the next tile's K as soon as S^T has consumed this
+    // tile's K; both are in flight during the softmax and P V of this tile.
+    u32x4 kc[TT][KS], vr[TT][KS];
+    bool cur_valid[TT];
+    if (tb < j1) {
+        locate_tile(tb);
+        load_k(kc);
+        load_v(vr);
+    }
 
     // new row i sits at T - q_len + i; rows see positions <= their own
     const int32_t P0 = s.T - p.q_len;
     const bool sink_window = p.mask_mode == MASK_SINK_WINDOW;
+    // per row tile: the row's last visible position and window start
+    int32_t hi[R], lo[R];
+#pragma unroll
+    for (int qt = 0; qt < R; ++qt) {
+        hi[qt] = P0 + row_i[qt];
+        lo[qt] = sink_window ? hi[qt] - p.window + 1 : 0;
+    }
+    const float c = p.scale_log2;
 
     for (; tb < j1; tb += step) {
         // stage this tile's V rows in LDS: [position][d], padded rows
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < TT; ++tt) {
+            cur_valid[tt] = pvalid[tt];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+                u32x4 v = vr[tt][ks];
+                if constexpr (CACHE == PAGED) {
+                    if (!pvalid[tt]) v = u32x4{0, 0, 0, 0};
+                }
                 char* dst = vbuf + (tt * 16 + lr) * VROW + (ks * 4 + lq) * 16;
-                *reinterpret_cast<uint2*>(dst) = uint2{vr[tt][ks][0], vr[tt][ks][1]};
-                *reinterpret_cast<uint2*>(dst + 8) = uint2{vr[tt][ks][2], vr[tt][ks][3]};
+                *reinterpret_cast<uint2*>(dst) = uint2{v[0], v[1]};
+                *reinterpret_cast<uint2*>(dst + 8) = uint2{v[2], v[3]};
             }
-        // prefetch the next tile
+        }
         const bool more = tb + step < j1;
-        if (more) load_tile(tb + step, kn, vr);
+        if (more) {
+            locate_tile(tb + step);
+            load_v(vr);
+        }
 
         // S^T = K . Q^T
-        f32x4 st[2][R];
+        f32x4 st[TT][R];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
             for (int qt = 0; qt < R; ++qt) {
                 f32x4 acc = {0, 0, 0, 0};
@@ -201,53 +257,77 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
                 for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32<DT>(kc[tt][ks], qf[qt][ks], acc);
                 st[tt][qt] = acc;
             }
+        if (more) load_k(kc);
 
-        // scale, mask, online softmax (per row: lane column lr of each row tile)
-        const bool edge = tb + TILE > j1 || (p.q_len > 1 && (sink_window ||
-                                                             span_pos(s, min(tb + TILE, j1) - 1) > P0));
-        uint32_t pf[R][4];
+        // Mask only where it can bite: a partial tile, rows that do not all see the
+        // tile's last position (q_len > 1), the window mask, or a bad page entry.
+        bool all_pages = true;
+        if constexpr (CACHE == PAGED) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) all_pages = all_pages && __all(cur_valid[tt]);
+        }
+        const bool edge = (tb + TILE > j1) || !all_pages ||
+                          (p.q_len > 1 && (sink_window ||
+                                           span_pos(s, min(tb + TILE, j1) - 1) > P0));
+        if (edge) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t j = tb + tt * 16 + lq * 4 + e;
+                    const int32_t pos = span_pos(s, min(j, j1 - 1));
+                    bool pv = true;
+                    if constexpr (CACHE == PAGED) {
+                        const int32_t blk = page_entry(p, b, pos);
+                        pv = (uint32_t)blk < (uint32_t)p.num_blocks;
+                    }
+#pragma unroll
+                    for (int qt = 0; qt < R; ++qt) {
+                        const bool ok = (j < j1) & pv & (pos <= hi[qt]) &
+                                        ((pos < p.n_sink) | (pos >= lo[qt]));
+                        st[tt][qt][e] = ok ? st[tt][qt][e] : NEG_INF;
+                    }
+                }
+            }
+        }
+
+        // online softmax per row (row = lane column lr of each row tile); scores
+        // stay raw, the scale enters through the exp2 argument
+        uint32_t pf[KK][R][4];
         bool rescale = false;
         float alpha[R];
 #pragma unroll
         for (int qt = 0; qt < R; ++qt) {
-            float x[2][4];
-            float mt = NEG_INF;
+            float mt = st[0][qt][0];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float v = st[tt][qt][e] * p.scale_log2;
-                    if (edge) {
-                        const int32_t j = tb + tt * 16 + lq * 4 + e;
-                        bool ok = j < j1;
-                        if (ok) ok = row_attends(p, s, row_i[qt], span_pos(s, j));
-                        v = ok ? v : NEG_INF;
-                    }
-                    x[tt][e] = v;
-                    mt = fmaxf(mt, v);
-                }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float m_new = fmaxf(m[qt], mt);
+                for (int e = 0; e < 4; ++e) mt = fmaxf(mt, st[tt][qt][e]);
+            mt = xmax_16_32(mt);
+            const float m_new = fmaxf(m[qt], mt * c);
             const float m_use = m_new == NEG_INF ? 0.0f : m_new;
             alpha[qt] = fast_exp2(m[qt] - m_use);
             rescale |= m_new != m[qt];
             m[qt] = m_new;
             float ps = 0.0f;
-            float pw[2][4];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int kk = 0; kk < KK; ++kk) {
+                float pw[2][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pw[tt][e] = fast_exp2(x[tt][e] - m_use);
-                    ps += pw[tt][e];
-                }
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pw[h][e] = fast_exp2(fmaf(st[2 * kk + h][qt][e], c, -m_use));
+                        ps += pw[h][e];
+                    }
+                // P^T operand of k-step kk: k = 8*lq + e -> positions kk*32 + 4*lq + e
+                // (first half) and kk*32 + 16 + 4*lq + e (second half)
+                pf[kk][qt][0] = pack2<DT>(pw[0][0], pw[0][1]);
+                pf[kk][qt][1] = pack2<DT>(pw[0][2], pw[0][3]);
+                pf[kk][qt][2] = pack2<DT>(pw[1][0], pw[1][1]);
+                pf[kk][qt][3] = pack2<DT>(pw[1][2], pw[1][3]);
+            }
             lsum[qt] = lsum[qt] * alpha[qt] + ps;
-            // P^T operand: k = 8*lq + e -> positions 4*lq+e (first half), 16+4*lq+e (second)
-            pf[qt][0] = pack2<DT>(pw[0][0], pw[0][1]);
-            pf[qt][1] = pack2<DT>(pw[0][2], pw[0][3]);
-            pf[qt][2] = pack2<DT>(pw[1][0], pw[1][1]);
-            pf[qt][3] = pack2<DT>(pw[1][2], pw[1][3]);
         }
         if (__any(rescale)) {
 #pragma unroll
@@ -259,42 +339,36 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
         // O^T += V^T . P^T, V^T read back transposed from LDS
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int dt = 0; dt < DT16; ++dt) {
-            const char* col = vbuf + (dt * 16 + lr) * 2;
-            uint32_t w[4];
+        for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const char* r0 = col + (h * 16 + lq * 4) * VROW;
-                const uint32_t a0 = *reinterpret_cast<const uint16_t*>(r0);
-                const uint32_t a1 = *reinterpret_cast<const uint16_t*>(r0 + VROW);
-                const uint32_t a2 = *reinterpret_cast<const uint16_t*>(r0 + 2 * VROW);
-                const uint32_t a3 = *reinterpret_cast<const uint16_t*>(r0 + 3 * VROW);
-                w[2 * h] = a0 | (a1 << 16);
-                w[2 * h + 1] = a2 | (a3 << 16);
-            }
-            const u32x4 va = {w[0], w[1], w[2], w[3]};
+            for (int dt = 0; dt < DT16; ++dt) {
+                const char* col = vbuf + (dt * 16 + lr) * 2;
+                uint32_t w[4];
 #pragma unroll
-            for (int qt = 0; qt < R; ++qt) {
-                const u32x4 pb = {pf[qt][0], pf[qt][1], pf[qt][2], pf[qt][3]};
-                o[dt][qt] = mfma16x16x32<DT>(va, pb, o[dt][qt]);
+                for (int h = 0; h < 2; ++h) {
+                    const char* r0 = col + (kk * 32 + h * 16 + lq * 4) * VROW;
+                    const uint32_t a0 = *reinterpret_cast<const uint16_t*>(r0);
+                    const uint32_t a1 = *reinterpret_cast<const uint16_t*>(r0 + VROW);
+                    const uint32_t a2 = *reinterpret_cast<const uint16_t*>(r0 + 2 * VROW);
+                    const uint32_t a3 = *reinterpret_cast<const uint16_t*>(r0 + 3 * VROW);
+                    w[2 * h] = a0 | (a1 << 16);
+                    w[2 * h + 1] = a2 | (a3 << 16);
+                }
+                const u32x4 va = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+                for (int qt = 0; qt < R; ++qt) {
+                    const u32x4 pb = {pf[kk][qt][0], pf[kk][qt][1], pf[kk][qt][2], pf[kk][qt][3]};
+                    o[dt][qt] = mfma16x16x32<DT>(va, pb, o[dt][qt]);
+                }
             }
         }
         __builtin_amdgcn_wave_barrier();
-
-        if (more) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kc[tt][ks] = kn[tt][ks];
-        }
     }
 
     // ---- merge the four waves: per row (m, l), then sum of rescaled O in LDS
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
-        float lt = lsum[qt];
-        lt += __shfl_xor(lt, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        const float lt = xsum_16_32(lsum[qt]);
         lsum[qt] = lt;
         if (lq == 0) {
             sm_m[wave][qt * 16 + lr] = m[qt];

@@ -247,6 +247,11 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
     }
     h->ws_rows = workspace_rows(*cfg);
     h->n_units = counter_units(*cfg);
+    // the merge addresses partials with 32-bit byte offsets
+    if ((double)h->ws_rows * cfg->head_dim * sizeof(float) >= 2147483648.0) {
+        delete h;
+        return fail(KVATTN_ERR_CAPACITY, "workspace would exceed 2 GiB; lower max_batch or max_q_len");
+    }
     const size_t bytes = workspace_size(*cfg, h->ws_rows);
     e = hipMalloc(reinterpret_cast<void**>(&h->ws), bytes);
     if (e != hipSuccess) {

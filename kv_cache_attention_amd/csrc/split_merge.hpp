@@ -44,9 +44,32 @@ __device__ __forceinline__ int64_t row_id_of(const DecodeParams& p, int b, int k
 __device__ __forceinline__ void store_partial(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_partial(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+
+// Vector loads of partials with the device-scope cache policy (SC1: the load is
+// served from the device-coherent level, never from a stale per-XCD L2 line),
+// through a buffer resource over the partial arrays (byte offsets < 2^31, which
+// the host guarantees by bounding the workspace).
+constexpr int kCachePolicyDevice = 16;  // SC1
+constexpr int kBufferDword3 = 0x00020000;
+
+struct PartialReader {
+    __amdgpu_buffer_rsrc_t acc, ml;
+    __device__ PartialReader(const DecodeParams& p)
+        : acc(__builtin_amdgcn_make_buffer_rsrc(p.ws_acc, 0, 0x7fffffff, kBufferDword3)),
+          ml(__builtin_amdgcn_make_buffer_rsrc(p.ws_ml, 0, 0x7fffffff, kBufferDword3)) {}
+    __device__ float4 acc4(int64_t float_index) const {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(acc, (int)(float_index * 4), 0,
+                                                             kCachePolicyDevice);
+        return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                      __uint_as_float(v[3])};
+    }
+    // (m, l) of partial `part`
+    __device__ float2 ml2(int64_t part) const {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ml, (int)(part * 8), 0,
+                                                            kCachePolicyDevice);
+        return float2{__uint_as_float(v[0]), __uint_as_float(v[1])};
+    }
+};
 
 // Shared memory the merge needs (floats).
 template <int NROWS, int THREADS>
@@ -74,24 +97,33 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
     constexpr int NW = THREADS / 64;
     const int wave = tid / 64, lane = tid % 64;
     const int n_split = p.n_split;
+    const PartialReader rd(p);
 
     // per row: M and L over the splits (one wave per row, lanes across splits)
     for (int r = wave; r < NROWS; r += NW) {
         const int rg = row0 + r;
         if (rg >= p.rows) continue;
-        const float* ml = p.ws_ml + row_id_of(p, b, kvh, rg) * n_split * 2;
-        float mx = NEG_INF;
-        for (int sp = lane; sp < nvalid; sp += 64) mx = fmaxf(mx, load_partial(ml + sp * 2));
+        const int64_t part0 = row_id_of(p, b, kvh, rg) * n_split;
+        float mx = NEG_INF, ls = 0.0f;
+        for (int sp = lane; sp < nvalid; sp += 64) {
+            // running (max, sum) over this lane's splits
+            const float2 v = rd.ml2(part0 + sp);
+            const float mn = fmaxf(mx, v.x);
+            const float mu = mn == NEG_INF ? 0.0f : mn;
+            ls = ls * fast_exp2(mx - mu) + v.y * fast_exp2(v.x - mu);
+            mx = mn;
+        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        const float mu = mx == NEG_INF ? 0.0f : mx;
-        float ls = 0.0f;
-        for (int sp = lane; sp < nvalid; sp += 64)
-            ls += load_partial(ml + sp * 2 + 1) * fast_exp2(load_partial(ml + sp * 2) - mu);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
+        for (int o = 32; o > 0; o >>= 1) {
+            const float mo = __shfl_xor(mx, o, 64);
+            const float lo = __shfl_xor(ls, o, 64);
+            const float mn = fmaxf(mx, mo);
+            const float mu = mn == NEG_INF ? 0.0f : mn;
+            ls = ls * fast_exp2(mx - mu) + lo * fast_exp2(mo - mu);
+            mx = mn;
+        }
         if (lane == 0) {
-            sm.M[r] = mu;
+            sm.M[r] = mx == NEG_INF ? 0.0f : mx;
             sm.L[r] = ls;
         }
     }
@@ -113,39 +145,34 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
         int64_t rid = 0;
         if (rg < p.rows) {
             rid = row_id_of(p, b, kvh, rg);
-            const float* ml = p.ws_ml + rid * n_split * 2;
-            const float* acc = p.ws_acc + rid * n_split * D + d4 * 4;
+            const int64_t part0 = rid * n_split;
             const float mu = sm.M[r];
-            auto ld4 = [&](int sp_) {
-                const float* q = acc + (int64_t)sp_ * D;
-                return float4{load_partial(q), load_partial(q + 1), load_partial(q + 2),
-                              load_partial(q + 3)};
-            };
             int sp = sg;
-            // four independent loads in flight per step
-            for (; sp + 3 * SG < nvalid; sp += 4 * SG) {
-                float4 v[4];
-                float w[4];
+            // eight independent vector loads in flight per step
+            for (; sp + 7 * SG < nvalid; sp += 8 * SG) {
+                float4 v[8];
+                float w[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    v[u] = ld4(sp + u * SG);
-                    w[u] = fast_exp2(load_partial(ml + (sp + u * SG) * 2) - mu);
+                for (int u = 0; u < 8; ++u) {
+                    v[u] = rd.acc4((part0 + sp + u * SG) * D + d4 * 4);
+                    w[u] = rd.ml2(part0 + sp + u * SG).x;
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    a.x += w[u] * v[u].x;
-                    a.y += w[u] * v[u].y;
-                    a.z += w[u] * v[u].z;
-                    a.w += w[u] * v[u].w;
+                for (int u = 0; u < 8; ++u) {
+                    const float f = fast_exp2(w[u] - mu);
+                    a.x += f * v[u].x;
+                    a.y += f * v[u].y;
+                    a.z += f * v[u].z;
+                    a.w += f * v[u].w;
                 }
             }
             for (; sp < nvalid; sp += SG) {
-                const float4 v = ld4(sp);
-                const float w = fast_exp2(load_partial(ml + sp * 2) - mu);
-                a.x += w * v.x;
-                a.y += w * v.y;
-                a.z += w * v.z;
-                a.w += w * v.w;
+                const float4 v = rd.acc4((part0 + sp) * D + d4 * 4);
+                const float f = fast_exp2(rd.ml2(part0 + sp).x - mu);
+                a.x += f * v.x;
+                a.y += f * v.y;
+                a.z += f * v.z;
+                a.w += f * v.w;
             }
         }
         if constexpr (SG > 1) {
