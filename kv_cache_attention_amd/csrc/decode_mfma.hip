@@ -8,14 +8,14 @@
 // run as v_mfma_f32_16x16x32_{bf16,f16} tiles with fp32 accumulation.
 //
 // One workgroup (4 wave64) owns a (sequence, KV head, split); each wave takes
-// every 4th tile of 64 positions (32 for 49-64 rows).  Per tile and wave:
-//   S^T[64 x rows] = K[64 x d] . Q^T[d x rows]   K straight from HBM into the
+// every 4th tile of 32 positions.  Per tile and wave:
+//   S^T[32 x rows] = K[32 x d] . Q^T[d x rows]   K straight from HBM into the
 //                     A operand (each lane's 16 bytes are 8 consecutive d of one
-//                     position: the operand layout), Q^T held in registers;
+//                     position: the operand layout), Q^T fragments in LDS;
 //   online softmax per row over the tile (running max / sum, as in the Flash
 //                     Attention section of the nextadmin.net lesson "KV cache
 //                     and Flash Attention"), P rounded to the input type;
-//   O^T[d x rows]  += V^T[d x 64] . P^T[64 x rows]   V needs positions along each
+//   O^T[d x rows]  += V^T[d x 32] . P^T[32 x rows]   V needs positions along each
 //                     lane's 8 operand elements while HBM holds it d-contiguous,
 //                     so V goes HBM -> registers -> LDS and is read back
 //                     transposed (2-byte reads from a padded, bank-conflict-free
@@ -41,13 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int MFMA_THREADS = 256;
 constexpr int MFMA_WAVES = MFMA_THREADS / 64;
-// Positions per wave step: 64 (32 when four row tiles leave too few registers).
-template <int R>
-struct MfmaTile {
-    static constexpr int TILE = R <= 3 ? 64 : 32;
-    static constexpr int TT = TILE / 16;  // 16-position sub-tiles (S^T accumulators)
-    static constexpr int KK = TILE / 32;  // 32-position k-steps of P V
-};
+constexpr int TILE = 32;  // positions per wave step (two 16-position halves, one P V k-step)
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -87,27 +81,35 @@ __device__ __forceinline__ float xsum_16_32(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-template <int D, int TILE>
+
+template <int D, int R>
 struct MfmaGeo {
-    static constexpr int KS = D / 32;                // k-steps of 32 along d
-    static constexpr int DT16 = D / 16;              // 16-wide d tiles of the output
-    static constexpr int VROW = D * 2 + 8;           // LDS bytes per staged V row (padded)
-    static constexpr int VBUF = TILE * VROW;         // LDS bytes per wave
+    static constexpr int KS = D / 32;          // k-steps of 32 along d (Q K^T)
+    static constexpr int DT16 = D / 16;        // 16-wide d tiles of the output
+    static constexpr int VROW = D * 2 + 16;    // LDS bytes per staged V row: 16-byte aligned,
+                                               // 4 dwords of padding keep reads and writes
+                                               // free of bank conflicts
+    static constexpr int VBUF = TILE * VROW;   // LDS bytes per wave
+    static constexpr int CPR = D * 2 / 16;     // 16-byte chunks per V row
+    static constexpr int PPI = 64 / CPR;       // V rows per wave-wide load
+    static constexpr int NV = TILE / PPI;      // V loads per lane per tile
+    static constexpr int QFRAGS = R * KS;      // Q^T operand fragments (64 lanes x 16 bytes)
 };
 
 template <int DT, int D, int R, int CACHE>
-__global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeParams p) {
-    constexpr int TILE = MfmaTile<R>::TILE, TT = MfmaTile<R>::TT, KK = MfmaTile<R>::KK;
-    using G = MfmaGeo<D, TILE>;
-    constexpr int KS = G::KS, DT16 = G::DT16, VROW = G::VROW;
+__global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? 2 : 1) void decode_mfma_kernel(const DecodeParams p) {
+    using G = MfmaGeo<D, R>;
+    constexpr int KS = G::KS, DT16 = G::DT16, VROW = G::VROW, CPR = G::CPR, PPI = G::PPI,
+                  NV = G::NV;
     constexpr float NEG_INF = -__builtin_inff();
     constexpr int NQ = R * 16;  // padded rows
 
-    // V staging (per wave) during the loop; reused for the cross-wave merge after it.
+    // V staging (per wave) during the loop, reused for the cross-wave merge after it;
+    // the Q^T operand fragments, shared by the four waves.
     constexpr int SMEM_V = MFMA_WAVES * G::VBUF;
-    constexpr int SMEM_O = NQ * D * 4;
-    static_assert(SMEM_O <= SMEM_V, "merge buffer must fit in the staging area");
+    static_assert(NQ * D * 4 <= SMEM_V, "merge buffer must fit in the staging area");
     __shared__ __attribute__((aligned(16))) char smem[SMEM_V];
+    __shared__ u32x4 qsm[G::QFRAGS * 64];
     __shared__ float sm_m[MFMA_WAVES][NQ];
     __shared__ float sm_l[MFMA_WAVES][NQ];
 
@@ -126,24 +128,7 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
     const int lr = l % 16;  // operand row / output column
     const int lq = l / 16;  // operand k-group / output row group
 
-    // Q^T operand fragments: row n = qt*16 + lr, d chunk (ks*4 + lq)*8.
-    u32x4 qf[R][KS];
-#pragma unroll
-    for (int qt = 0; qt < R; ++qt) {
-        const int n = qt * 16 + lr;
-        const bool ok = n < p.rows;
-        const int i = ok ? n / p.group : 0;
-        const int h = kvh * p.group + (ok ? n - i * p.group : 0);
-        const int64_t base = (((int64_t)b * p.q_len + i) * p.num_q_heads + h) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int64_t off = base + (ks * 4 + lq) * 8;
-            qf[qt][ks] = ok ? *reinterpret_cast<const u32x4*>(
-                                  reinterpret_cast<const uint16_t*>(p.q) + off)
-                            : u32x4{0, 0, 0, 0};
-        }
-    }
-    // rows' new-token index (for the causal / window mask), -1 for padding rows
+    // rows' new-token index (for the causal / window mask); padding rows act as the last
     int row_i[R];
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
@@ -167,55 +152,76 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
     const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k);
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v);
 
-    // K and V of one tile, in the A-operand lane mapping: position tile + tt*16 + lr,
-    // d chunk (ks*4 + lq)*8.  Loads are branch-free: a position past the split is
-    // clamped to the split's last one (an attended, finite row) and its scores are
-    // masked; a paged position behind an out-of-pool entry reads block 0 and both
-    // its score and its V are discarded by selects.
-    bool pvalid[TT];
-    int64_t offs[TT];
-    auto locate_tile = [&](int32_t tb) {
+    // Loads are branch-free: a position past the split is clamped to the split's last
+    // one (an attended, finite row) and its scores are masked; a paged position behind
+    // an out-of-pool entry reads block 0 and both its score and its V are discarded.
+    // K in the A-operand lane mapping: position tile + tt*16 + lr, d chunk (ks*4+lq)*8.
+    auto load_k = [&](int32_t tb, u32x4 (&kf)[2][KS]) {
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
+        for (int tt = 0; tt < 2; ++tt) {
             const int32_t j = min(tb + tt * 16 + lr, j1 - 1);
             Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
-            pvalid[tt] = L.unit >= 0;
             L.unit = L.unit >= 0 ? L.unit : 0;
-            offs[tt] = row_offset(p, L, kvh);
+            const int64_t off = row_offset(p, L, kvh) + lq * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[tt][ks] = *reinterpret_cast<const u32x4*>(kp + off + ks * 32);
         }
     };
-    auto load_k = [&](u32x4 (&kf)[TT][KS]) {
+    // V coalesced: load v covers PPI whole rows, lane l -> row v*PPI + l/CPR, chunk l%CPR.
+    bool vok[NV];
+    auto load_v = [&](int32_t tb, u32x4 (&vf)[NV]) {
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[tt][ks] = *reinterpret_cast<const u32x4*>(kp + offs[tt] + (ks * 4 + lq) * 8);
-    };
-    auto load_v = [&](u32x4 (&vf)[TT][KS]) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                vf[tt][ks] = *reinterpret_cast<const u32x4*>(vp + offs[tt] + (ks * 4 + lq) * 8);
+        for (int v = 0; v < NV; ++v) {
+            const int32_t j = min(tb + v * PPI + l / CPR, j1 - 1);
+            Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
+            vok[v] = L.unit >= 0;
+            L.unit = L.unit >= 0 ? L.unit : 0;
+            vf[v] = *reinterpret_cast<const u32x4*>(vp + row_offset(p, L, kvh) + (l % CPR) * 8);
+        }
     };
 
     const int32_t step = MFMA_WAVES * TILE;
     int32_t tb = j0 + wave * TILE;
-    // One register buffer each for K and V.  The next tile's V is loaded as soon as
-    // this tile's V is in LDS, the next tile's K as soon as S^T has consumed this
-    // tile's K; both are in flight during the softmax and P V of this tile.
-    u32x4 kc[TT][KS], vr[TT][KS];
-    bool cur_valid[TT];
-    if (tb < j1) {
-        locate_tile(tb);
-        load_k(kc);
-        load_v(vr);
+    // One register buffer each for K and V: the next tile's V is loaded as soon as
+    // this tile's V sits in LDS, the next K as soon as S^T has consumed this K.
+    // Q^T operand fragments (LDS): fragment f = qt*KS + ks; lane l holds row
+    // qt*16 + l%16, d chunk (ks*4 + l/16)*8.  Loaded first, stored after the first
+    // tile's loads are in flight.
+    constexpr int QPT = (G::QFRAGS * 64 + MFMA_THREADS - 1) / MFMA_THREADS;
+    u32x4 qreg[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const int idx = tid + k * MFMA_THREADS;
+        const int f = idx / 64, ll = idx % 64;
+        const int qt = f / KS, ks = f % KS;
+        const int n = qt * 16 + ll % 16;
+        qreg[k] = u32x4{0, 0, 0, 0};
+        if (idx < G::QFRAGS * 64 && n < p.rows) {
+            const int i = n / p.group;
+            const int h = kvh * p.group + (n - i * p.group);
+            const int64_t off = (((int64_t)b * p.q_len + i) * p.num_q_heads + h) * D +
+                                (ks * 4 + ll / 16) * 8;
+            qreg[k] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + off);
+        }
     }
+
+    u32x4 kc[2][KS], vr[NV];
+    if (tb < j1) {
+        load_k(tb, kc);
+        load_v(tb, vr);
+    }
+
+    // Q staged from registers once the loads above are issued (the Q loads were
+    // issued first, so waiting for them does not wait for the tile)
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (tid + k * MFMA_THREADS < G::QFRAGS * 64) qsm[tid + k * MFMA_THREADS] = qreg[k];
+    __syncthreads();
 
     // new row i sits at T - q_len + i; rows see positions <= their own
     const int32_t P0 = s.T - p.q_len;
     const bool sink_window = p.mask_mode == MASK_SINK_WINDOW;
-    // per row tile: the row's last visible position and window start
     int32_t hi[R], lo[R];
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
@@ -225,53 +231,45 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
     const float c = p.scale_log2;
 
     for (; tb < j1; tb += step) {
-        // stage this tile's V rows in LDS: [position][d], padded rows
+        // stage this tile's V rows in LDS: [position][d], padded rows, 16-byte writes
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            cur_valid[tt] = pvalid[tt];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 v = vr[tt][ks];
-                if constexpr (CACHE == PAGED) {
-                    if (!pvalid[tt]) v = u32x4{0, 0, 0, 0};
-                }
-                char* dst = vbuf + (tt * 16 + lr) * VROW + (ks * 4 + lq) * 16;
-                *reinterpret_cast<uint2*>(dst) = uint2{v[0], v[1]};
-                *reinterpret_cast<uint2*>(dst + 8) = uint2{v[2], v[3]};
+        for (int v = 0; v < NV; ++v) {
+            u32x4 x = vr[v];
+            if constexpr (CACHE == PAGED) {
+                if (!vok[v]) x = u32x4{0, 0, 0, 0};
             }
+            *reinterpret_cast<u32x4*>(vbuf + (v * PPI + l / CPR) * VROW + (l % CPR) * 16) = x;
         }
         const bool more = tb + step < j1;
-        if (more) {
-            locate_tile(tb + step);
-            load_v(vr);
-        }
+        if (more) load_v(tb + step, vr);
 
         // S^T = K . Q^T
-        f32x4 st[TT][R];
+        f32x4 st[2][R];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int qt = 0; qt < R; ++qt) {
                 f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32<DT>(kc[tt][ks], qf[qt][ks], acc);
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = mfma16x16x32<DT>(kc[tt][ks], qsm[(qt * KS + ks) * 64 + l], acc);
                 st[tt][qt] = acc;
             }
-        if (more) load_k(kc);
+        if (more) load_k(tb + step, kc);
 
         // Mask only where it can bite: a partial tile, rows that do not all see the
-        // tile's last position (q_len > 1), the window mask, or a bad page entry.
-        bool all_pages = true;
+        // tile's last position (q_len > 1), the window mask, or (paged) a bad entry.
+        bool edge = (tb + TILE > j1) ||
+                    (p.q_len > 1 && (sink_window || span_pos(s, min(tb + TILE, j1) - 1) > P0));
         if constexpr (CACHE == PAGED) {
+            bool bad = false;
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) all_pages = all_pages && __all(cur_valid[tt]);
+            for (int v = 0; v < NV; ++v) bad = bad || !vok[v];
+            edge = edge || __any(bad);
         }
-        const bool edge = (tb + TILE > j1) || !all_pages ||
-                          (p.q_len > 1 && (sink_window ||
-                                           span_pos(s, min(tb + TILE, j1) - 1) > P0));
         if (edge) {
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
+            for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int32_t j = tb + tt * 16 + lq * 4 + e;
@@ -291,16 +289,16 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
             }
         }
 
-        // online softmax per row (row = lane column lr of each row tile); scores
-        // stay raw, the scale enters through the exp2 argument
-        uint32_t pf[KK][R][4];
+        // online softmax per row (row = lane column lr of each row tile); scores stay
+        // raw, the scale enters through the exp2 argument
+        uint32_t pf[R][4];
         bool rescale = false;
         float alpha[R];
 #pragma unroll
         for (int qt = 0; qt < R; ++qt) {
             float mt = st[0][qt][0];
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mt = fmaxf(mt, st[tt][qt][e]);
             mt = xmax_16_32(mt);
@@ -309,25 +307,21 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
             alpha[qt] = fast_exp2(m[qt] - m_use);
             rescale |= m_new != m[qt];
             m[qt] = m_new;
+            float pw[2][4];
             float ps = 0.0f;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                float pw[2][4];
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pw[h][e] = fast_exp2(fmaf(st[2 * kk + h][qt][e], c, -m_use));
-                        ps += pw[h][e];
-                    }
-                // P^T operand of k-step kk: k = 8*lq + e -> positions kk*32 + 4*lq + e
-                // (first half) and kk*32 + 16 + 4*lq + e (second half)
-                pf[kk][qt][0] = pack2<DT>(pw[0][0], pw[0][1]);
-                pf[kk][qt][1] = pack2<DT>(pw[0][2], pw[0][3]);
-                pf[kk][qt][2] = pack2<DT>(pw[1][0], pw[1][1]);
-                pf[kk][qt][3] = pack2<DT>(pw[1][2], pw[1][3]);
-            }
+                for (int e = 0; e < 4; ++e) {
+                    pw[tt][e] = fast_exp2(fmaf(st[tt][qt][e], c, -m_use));
+                    ps += pw[tt][e];
+                }
             lsum[qt] = lsum[qt] * alpha[qt] + ps;
+            // P^T operand: k = 8*lq + e -> positions 4*lq+e (first half), 16+4*lq+e (second)
+            pf[qt][0] = pack2<DT>(pw[0][0], pw[0][1]);
+            pf[qt][1] = pack2<DT>(pw[0][2], pw[0][3]);
+            pf[qt][2] = pack2<DT>(pw[1][0], pw[1][1]);
+            pf[qt][3] = pack2<DT>(pw[1][2], pw[1][3]);
         }
         if (__any(rescale)) {
 #pragma unroll
@@ -336,30 +330,28 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
                 for (int qt = 0; qt < R; ++qt) o[dt][qt] *= alpha[qt];
         }
 
-        // O^T += V^T . P^T, V^T read back transposed from LDS
+        // O^T += V^T . P^T, V^T read back transposed from LDS with the same position
+        // permutation as P^T
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int dt = 0; dt < DT16; ++dt) {
+            const char* col = vbuf + (dt * 16 + lr) * 2;
+            uint32_t w[4];
 #pragma unroll
-            for (int dt = 0; dt < DT16; ++dt) {
-                const char* col = vbuf + (dt * 16 + lr) * 2;
-                uint32_t w[4];
+            for (int h = 0; h < 2; ++h) {
+                const char* r0 = col + (h * 16 + lq * 4) * VROW;
+                const uint32_t a0 = *reinterpret_cast<const uint16_t*>(r0);
+                const uint32_t a1 = *reinterpret_cast<const uint16_t*>(r0 + VROW);
+                const uint32_t a2 = *reinterpret_cast<const uint16_t*>(r0 + 2 * VROW);
+                const uint32_t a3 = *reinterpret_cast<const uint16_t*>(r0 + 3 * VROW);
+                w[2 * h] = a0 | (a1 << 16);
+                w[2 * h + 1] = a2 | (a3 << 16);
+            }
+            const u32x4 va = {w[0], w[1], w[2], w[3]};
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const char* r0 = col + (kk * 32 + h * 16 + lq * 4) * VROW;
-                    const uint32_t a0 = *reinterpret_cast<const uint16_t*>(r0);
-                    const uint32_t a1 = *reinterpret_cast<const uint16_t*>(r0 + VROW);
-                    const uint32_t a2 = *reinterpret_cast<const uint16_t*>(r0 + 2 * VROW);
-                    const uint32_t a3 = *reinterpret_cast<const uint16_t*>(r0 + 3 * VROW);
-                    w[2 * h] = a0 | (a1 << 16);
-                    w[2 * h + 1] = a2 | (a3 << 16);
-                }
-                const u32x4 va = {w[0], w[1], w[2], w[3]};
-#pragma unroll
-                for (int qt = 0; qt < R; ++qt) {
-                    const u32x4 pb = {pf[kk][qt][0], pf[kk][qt][1], pf[kk][qt][2], pf[kk][qt][3]};
-                    o[dt][qt] = mfma16x16x32<DT>(va, pb, o[dt][qt]);
-                }
+            for (int qt = 0; qt < R; ++qt) {
+                const u32x4 pb = {pf[qt][0], pf[qt][1], pf[qt][2], pf[qt][3]};
+                o[dt][qt] = mfma16x16x32<DT>(va, pb, o[dt][qt]);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -376,55 +368,62 @@ __global__ __launch_bounds__(MFMA_THREADS) void decode_mfma_kernel(const DecodeP
         }
     }
     __syncthreads();  // also: every wave is done with its V staging area
-    float f[R];
-#pragma unroll
-    for (int qt = 0; qt < R; ++qt) {
-        const int n = qt * 16 + lr;
+    // per row: the workgroup's max M and sum L, and each wave's factor 2^(m_w - M)
+    __shared__ float sm_f[MFMA_WAVES][NQ];
+    __shared__ float sm_M[NQ], sm_L[NQ];
+    if (tid < NQ) {
         float M = NEG_INF;
 #pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, sm_m[w][n]);
+        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, sm_m[w][tid]);
         const float Mu = M == NEG_INF ? 0.0f : M;
-        f[qt] = fast_exp2(m[qt] - Mu);
+        float L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) {
+            const float f = fast_exp2(sm_m[w][tid] - Mu);
+            sm_f[w][tid] = f;
+            L += sm_l[w][tid] * f;
+        }
+        sm_M[tid] = M;
+        sm_L[tid] = L;
     }
+    __syncthreads();
     float* osum = reinterpret_cast<float*>(smem);  // [NQ][D]
     for (int w = 0; w < MFMA_WAVES; ++w) {
         if (wave == w) {
 #pragma unroll
             for (int dt = 0; dt < DT16; ++dt)
 #pragma unroll
-                for (int qt = 0; qt < R; ++qt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float* dst = osum + (qt * 16 + lr) * D + dt * 16 + lq * 4 + e;
-                        const float v = o[dt][qt][e] * f[qt];
-                        *dst = w == 0 ? v : *dst + v;
+                for (int qt = 0; qt < R; ++qt) {
+                    const float f = sm_f[w][qt * 16 + lr];
+                    float4* dst =
+                        reinterpret_cast<float4*>(osum + (qt * 16 + lr) * D + dt * 16 + lq * 4);
+                    const f32x4 v = o[dt][qt] * f;
+                    if (w == 0) {
+                        *dst = float4{v[0], v[1], v[2], v[3]};
+                    } else {
+                        const float4 a = *dst;
+                        *dst = float4{a.x + v[0], a.y + v[1], a.z + v[2], a.w + v[3]};
                     }
+                }
         }
         __syncthreads();
     }
-    // rows out: thread -> (row, d)
-    for (int idx = tid; idx < NQ * D; idx += MFMA_THREADS) {
-        const int n = idx / D;
-        const int d = idx - n * D;
+    // rows out, four d at a time: the final rows (one split) or this split's partial
+    for (int idx = tid; idx < NQ * D / 4; idx += MFMA_THREADS) {
+        const int n = idx / (D / 4);
+        const int d = (idx - n * (D / 4)) * 4;
         if (n >= p.rows) continue;
-        float M = NEG_INF;
-#pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, sm_m[w][n]);
-        const float Mu = M == NEG_INF ? 0.0f : M;
-        float L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) L += sm_l[w][n] * fast_exp2(sm_m[w][n] - Mu);
-        const float A = osum[idx];
+        const float4 A = *reinterpret_cast<const float4*>(osum + n * D + d);
         const int64_t rid = row_id_of(p, b, kvh, n);
         if (nvalid == 1) {
-            store_elem<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
+            const float L = sm_L[n];
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            const uint2 w = {pack2<DT>(A.x * inv, A.y * inv), pack2<DT>(A.z * inv, A.w * inv)};
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
         } else {
             const int64_t part = rid * p.n_split + split;
-            store_partial(p.ws_acc + part * D + d, A);
-            if (d == 0) {
-                store_partial(p.ws_ml + part * 2, M);
-                store_partial(p.ws_ml + part * 2 + 1, L);
-            }
+            store_partial4(p, part * D + d, A);
+            if (d == 0) store_partial_ml(p, part, sm_M[n], sm_L[n]);
         }
     }
     if (nvalid > 1) {

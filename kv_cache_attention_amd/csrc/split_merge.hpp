@@ -52,6 +52,25 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
 constexpr int kCachePolicyDevice = 16;  // SC1
 constexpr int kBufferDword3 = 0x00020000;
 
+// Vector device-scope partial stores (same buffer resources as the reader).
+__device__ __forceinline__ void store_partial4(const DecodeParams& p, int64_t float_index,
+                                               float4 v) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(p.ws_acc, 0, 0x7fffffff, 0x00020000);
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const u4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                  __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(float_index * 4), 0, 16);
+}
+__device__ __forceinline__ void store_partial_ml(const DecodeParams& p, int64_t part, float m,
+                                                 float l) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(p.ws_ml, 0, 0x7fffffff, 0x00020000);
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 w = {__float_as_uint(m), __float_as_uint(l)};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)(part * 8), 0, 16);
+}
+
 struct PartialReader {
     __amdgpu_buffer_rsrc_t acc, ml;
     __device__ PartialReader(const DecodeParams& p)
@@ -94,27 +113,38 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
     if (!s_last) return;
 
     constexpr float NEG_INF = -__builtin_inff();
-    constexpr int NW = THREADS / 64;
-    const int wave = tid / 64, lane = tid % 64;
     const int n_split = p.n_split;
     const PartialReader rd(p);
 
-    // per row: M and L over the splits (one wave per row, lanes across splits)
-    for (int r = wave; r < NROWS; r += NW) {
-        const int rg = row0 + r;
-        if (rg >= p.rows) continue;
-        const int64_t part0 = row_id_of(p, b, kvh, rg) * n_split;
+    // per row: M and L over the splits.  G lanes per row (aligned groups within a
+    // wave) each fold every G-th split, loads issued in batches, then the group
+    // combines its running (max, sum) pairs with shuffles.
+    constexpr int G0 = THREADS / NROWS >= 64 ? 64 : THREADS / NROWS;
+    constexpr int G = G0 >= 32 ? G0 : (G0 >= 16 ? 16 : (G0 >= 8 ? 8 : (G0 >= 4 ? 4 : (G0 >= 2 ? 2 : 1))));
+    static_assert(NROWS * G <= THREADS, "row groups");
+    {
+        const int r = tid / G, g = tid % G;
+        const bool act = r < NROWS && row0 + r < p.rows;
+        const int64_t part0 = act ? row_id_of(p, b, kvh, row0 + r) * n_split : 0;
         float mx = NEG_INF, ls = 0.0f;
-        for (int sp = lane; sp < nvalid; sp += 64) {
-            // running (max, sum) over this lane's splits
-            const float2 v = rd.ml2(part0 + sp);
-            const float mn = fmaxf(mx, v.x);
-            const float mu = mn == NEG_INF ? 0.0f : mn;
-            ls = ls * fast_exp2(mx - mu) + v.y * fast_exp2(v.x - mu);
-            mx = mn;
+        for (int sp0 = g; sp0 < nvalid; sp0 += 8 * G) {
+            float2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = sp0 + u * G;
+                v[u] = rd.ml2(part0 + (sp < nvalid ? sp : g));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (sp0 + u * G >= nvalid) continue;
+                const float mn = fmaxf(mx, v[u].x);
+                const float mu = mn == NEG_INF ? 0.0f : mn;
+                ls = ls * fast_exp2(mx - mu) + v[u].y * fast_exp2(v[u].x - mu);
+                mx = mn;
+            }
         }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
+        for (int o = G / 2; o > 0; o >>= 1) {
             const float mo = __shfl_xor(mx, o, 64);
             const float lo = __shfl_xor(ls, o, 64);
             const float mn = fmaxf(mx, mo);
@@ -122,80 +152,86 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
             ls = ls * fast_exp2(mx - mu) + lo * fast_exp2(mo - mu);
             mx = mn;
         }
-        if (lane == 0) {
+        if (act && g == 0) {
             sm.M[r] = mx == NEG_INF ? 0.0f : mx;
             sm.L[r] = ls;
         }
     }
     __syncthreads();
 
-    // accumulators: float4 chunks of (row, d); split groups share the remaining threads
+    // accumulators: float4 chunks of (row, d); split groups share the remaining threads.
+    // Every load of a step is issued before any is used (4 splits x EPT chunks), so
+    // the merge costs a few memory latencies, not one per split.
     constexpr int E4 = NROWS * D / 4;
     constexpr int SG = E4 >= THREADS ? 1 : THREADS / E4;
     constexpr int EPT = E4 >= THREADS ? E4 / THREADS : 1;
+    constexpr int US = 4;  // splits per step
     static_assert(E4 >= THREADS ? E4 % THREADS == 0 : THREADS % E4 == 0, "shape");
     const int sg = E4 >= THREADS ? 0 : tid / E4;
+    int e4[EPT], r[EPT];
+    bool live[EPT];
+    int64_t part0[EPT];
+    float mu[EPT];
+    float4 a[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        const int e4 = E4 >= THREADS ? tid + k * THREADS : tid % E4;
-        const int r = e4 / (D / 4);
-        const int d4 = e4 - r * (D / 4);
-        const int rg = row0 + r;
-        float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-        int64_t rid = 0;
-        if (rg < p.rows) {
-            rid = row_id_of(p, b, kvh, rg);
-            const int64_t part0 = rid * n_split;
-            const float mu = sm.M[r];
-            int sp = sg;
-            // eight independent vector loads in flight per step
-            for (; sp + 7 * SG < nvalid; sp += 8 * SG) {
-                float4 v[8];
-                float w[8];
+        e4[k] = E4 >= THREADS ? tid + k * THREADS : tid % E4;
+        r[k] = e4[k] / (D / 4);
+        live[k] = row0 + r[k] < p.rows;
+        part0[k] = live[k] ? row_id_of(p, b, kvh, row0 + r[k]) * n_split : 0;
+        mu[k] = live[k] ? sm.M[r[k]] : 0.0f;
+        a[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int sp0 = sg; sp0 < nvalid; sp0 += US * SG) {
+        float4 v[US][EPT];
+        float w[US][EPT];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    v[u] = rd.acc4((part0 + sp + u * SG) * D + d4 * 4);
-                    w[u] = rd.ml2(part0 + sp + u * SG).x;
-                }
+        for (int u = 0; u < US; ++u) {
+            const int sp = sp0 + u * SG;
+            const int spc = sp < nvalid ? sp : sg;  // clamped: a valid partial, weight 0
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float f = fast_exp2(w[u] - mu);
-                    a.x += f * v[u].x;
-                    a.y += f * v[u].y;
-                    a.z += f * v[u].z;
-                    a.w += f * v[u].w;
-                }
-            }
-            for (; sp < nvalid; sp += SG) {
-                const float4 v = rd.acc4((part0 + sp) * D + d4 * 4);
-                const float f = fast_exp2(rd.ml2(part0 + sp).x - mu);
-                a.x += f * v.x;
-                a.y += f * v.y;
-                a.z += f * v.z;
-                a.w += f * v.w;
+            for (int k = 0; k < EPT; ++k) {
+                const int64_t part = part0[k] + spc;
+                v[u][k] = rd.acc4(part * D + (e4[k] % (D / 4)) * 4);
+                w[u][k] = rd.ml2(part).x;
             }
         }
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const bool in = sp0 + u * SG < nvalid;
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const float f = in ? fast_exp2(w[u][k] - mu[k]) : 0.0f;
+                a[k].x += f * v[u][k].x;
+                a[k].y += f * v[u][k].y;
+                a[k].z += f * v[u][k].z;
+                a[k].w += f * v[u][k].w;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
         if constexpr (SG > 1) {
-            sm.red[tid] = a;
+            sm.red[tid] = a[k];
             __syncthreads();
-            if (sg == 0 && rg < p.rows) {
+            if (sg == 0) {
                 for (int g2 = 1; g2 < SG; ++g2) {
-                    const float4 o = sm.red[g2 * E4 + e4];
-                    a.x += o.x;
-                    a.y += o.y;
-                    a.z += o.z;
-                    a.w += o.w;
+                    const float4 o = sm.red[g2 * E4 + e4[k]];
+                    a[k].x += o.x;
+                    a[k].y += o.y;
+                    a[k].z += o.z;
+                    a[k].w += o.w;
                 }
             }
         }
-        if (sg == 0 && rg < p.rows) {
-            const float L = sm.L[r];
+        if (sg == 0 && live[k]) {
+            const float L = sm.L[r[k]];
             const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-            const int64_t o = rid * D + d4 * 4;
-            store_elem<DT>(p.out, o, a.x * inv);
-            store_elem<DT>(p.out, o + 1, a.y * inv);
-            store_elem<DT>(p.out, o + 2, a.z * inv);
-            store_elem<DT>(p.out, o + 3, a.w * inv);
+            const int64_t o = (part0[k] / n_split) * D + (e4[k] % (D / 4)) * 4;
+            store_elem<DT>(p.out, o, a[k].x * inv);
+            store_elem<DT>(p.out, o + 1, a[k].y * inv);
+            store_elem<DT>(p.out, o + 2, a[k].z * inv);
+            store_elem<DT>(p.out, o + 3, a[k].w * inv);
         }
     }
     if (tid == 0) atomicExch(p.counters + unit, 0);  // ready for the next call
