@@ -143,7 +143,7 @@ KVATTN_API int kvattn_set_split_len(kvattn_handle* h, int32_t split_len);
 /* The decomposition a decode with these host arguments would use:
  * n_split work items per (sequence, KV head) of split_len positions each, and
  * the kernel family (0 = vector-ALU rows, 1 = matrix-core rows). */
-KVATTN_API int kvattn_plan(const kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
+KVATTN_API int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
                 int32_t window, int32_t* n_split, int32_t* split_len, int32_t* kernel);
 
 /* Device bytes kvattn_create would allocate for `cfg`. */

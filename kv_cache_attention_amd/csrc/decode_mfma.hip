@@ -442,37 +442,40 @@ bool mfma_supported(int dtype, int head_dim, int rows) {
 }
 
 template <int DT, int D, int R>
-static hipError_t launch_mfma_c(const DecodeParams& p, hipStream_t st) {
-    dim3 grid(p.n_split, p.num_kv_heads, p.batch);
-    switch (p.cache_mode) {
-    case CONTIGUOUS:
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, D, R, CONTIGUOUS>), grid, dim3(MFMA_THREADS), 0, st, p);
-        break;
-    case PAGED:
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, D, R, PAGED>), grid, dim3(MFMA_THREADS), 0, st, p);
-        break;
-    default:
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, D, R, RING>), grid, dim3(MFMA_THREADS), 0, st, p);
-        break;
+static const void* mfma_kernel_c(int cache_mode) {
+    switch (cache_mode) {
+    case CONTIGUOUS: return reinterpret_cast<const void*>(&decode_mfma_kernel<DT, D, R, CONTIGUOUS>);
+    case PAGED: return reinterpret_cast<const void*>(&decode_mfma_kernel<DT, D, R, PAGED>);
+    default: return reinterpret_cast<const void*>(&decode_mfma_kernel<DT, D, R, RING>);
     }
-    return hipGetLastError();
 }
 
 template <int DT, int D>
-static hipError_t launch_mfma_r(const DecodeParams& p, hipStream_t st) {
-    switch ((p.rows + 15) / 16) {
-    case 1: return launch_mfma_c<DT, D, 1>(p, st);
-    case 2: return launch_mfma_c<DT, D, 2>(p, st);
-    case 3: return launch_mfma_c<DT, D, 3>(p, st);
-    default: return launch_mfma_c<DT, D, 4>(p, st);
+static const void* mfma_kernel_r(int rows, int cache_mode) {
+    switch ((rows + 15) / 16) {
+    case 1: return mfma_kernel_c<DT, D, 1>(cache_mode);
+    case 2: return mfma_kernel_c<DT, D, 2>(cache_mode);
+    case 3: return mfma_kernel_c<DT, D, 3>(cache_mode);
+    default: return mfma_kernel_c<DT, D, 4>(cache_mode);
     }
 }
 
-hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
-    if (!mfma_supported(dtype, head_dim, p.rows)) return hipErrorInvalidValue;
+const void* select_mfma_kernel(int dtype, int head_dim, int rows, int cache_mode) {
+    if (!mfma_supported(dtype, head_dim, rows)) return nullptr;
     if (dtype == F16)
-        return head_dim == 128 ? launch_mfma_r<F16, 128>(p, st) : launch_mfma_r<F16, 64>(p, st);
-    return head_dim == 128 ? launch_mfma_r<BF16, 128>(p, st) : launch_mfma_r<BF16, 64>(p, st);
+        return head_dim == 128 ? mfma_kernel_r<F16, 128>(rows, cache_mode)
+                               : mfma_kernel_r<F16, 64>(rows, cache_mode);
+    return head_dim == 128 ? mfma_kernel_r<BF16, 128>(rows, cache_mode)
+                           : mfma_kernel_r<BF16, 64>(rows, cache_mode);
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
+    const void* k = select_mfma_kernel(dtype, head_dim, p.rows, p.cache_mode);
+    if (!k) return hipErrorInvalidValue;
+    DecodeParams pp = p;
+    void* args[] = {&pp};
+    return hipLaunchKernel(k, dim3(p.n_split, p.num_kv_heads, p.batch), dim3(MFMA_THREADS), args,
+                           0, st);
 }
 
 }  // namespace kvattn

@@ -322,38 +322,33 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
 #define KVATTN_VALU_U_LARGE 4   // 8 or 16 rows
 #endif
 
+// Kernel selection: one instance per (dtype, head_dim, row bucket, cache form,
+// per-row mask); launches and occupancy queries go through the same choice.
 template <int DT, int D, int ROWS, int CACHE>
-static hipError_t launch_valu_t(const DecodeParams& p, int row_blocks, hipStream_t st) {
+static const void* valu_kernel_t(bool masked) {
     constexpr int U = ROWS <= 2 ? KVATTN_VALU_U_SMALL
                                 : (ROWS <= 4 ? KVATTN_VALU_U_MID : KVATTN_VALU_U_LARGE);
-    dim3 grid(p.n_split, p.num_kv_heads, p.batch * row_blocks);
-    if (p.q_len > 1)
-        hipLaunchKernelGGL((decode_valu_kernel<DT, D, ROWS, CACHE, U, true>), grid,
-                           dim3(VALU_THREADS), 0, st, p, row_blocks);
-    else
-        hipLaunchKernelGGL((decode_valu_kernel<DT, D, ROWS, CACHE, U, false>), grid,
-                           dim3(VALU_THREADS), 0, st, p, row_blocks);
-    return hipGetLastError();
+    return masked ? reinterpret_cast<const void*>(&decode_valu_kernel<DT, D, ROWS, CACHE, U, true>)
+                  : reinterpret_cast<const void*>(&decode_valu_kernel<DT, D, ROWS, CACHE, U, false>);
 }
 
 template <int DT, int D, int ROWS>
-static hipError_t launch_valu_c(const DecodeParams& p, int row_blocks, hipStream_t st) {
-    switch (p.cache_mode) {
-    case CONTIGUOUS: return launch_valu_t<DT, D, ROWS, CONTIGUOUS>(p, row_blocks, st);
-    case PAGED: return launch_valu_t<DT, D, ROWS, PAGED>(p, row_blocks, st);
-    default: return launch_valu_t<DT, D, ROWS, RING>(p, row_blocks, st);
+static const void* valu_kernel_c(int cache_mode, bool masked) {
+    switch (cache_mode) {
+    case CONTIGUOUS: return valu_kernel_t<DT, D, ROWS, CONTIGUOUS>(masked);
+    case PAGED: return valu_kernel_t<DT, D, ROWS, PAGED>(masked);
+    default: return valu_kernel_t<DT, D, ROWS, RING>(masked);
     }
 }
 
 template <int DT, int D>
-static hipError_t launch_valu_r(const DecodeParams& p, int rows_per_block, int row_blocks,
-                                hipStream_t st) {
+static const void* valu_kernel_r(int rows_per_block, int cache_mode, bool masked) {
     switch (rows_per_block) {
-    case 1: return launch_valu_c<DT, D, 1>(p, row_blocks, st);
-    case 2: return launch_valu_c<DT, D, 2>(p, row_blocks, st);
-    case 4: return launch_valu_c<DT, D, 4>(p, row_blocks, st);
-    case 8: return launch_valu_c<DT, D, 8>(p, row_blocks, st);
-    default: return launch_valu_c<DT, D, 16>(p, row_blocks, st);
+    case 1: return valu_kernel_c<DT, D, 1>(cache_mode, masked);
+    case 2: return valu_kernel_c<DT, D, 2>(cache_mode, masked);
+    case 4: return valu_kernel_c<DT, D, 4>(cache_mode, masked);
+    case 8: return valu_kernel_c<DT, D, 8>(cache_mode, masked);
+    default: return valu_kernel_c<DT, D, 16>(cache_mode, masked);
     }
 }
 
@@ -365,21 +360,30 @@ int valu_rows_per_block(int rows) {
     return 16;
 }
 
-hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
-    const int rpb = valu_rows_per_block(p.rows);
-    const int row_blocks = (p.rows + rpb - 1) / rpb;
+const void* select_valu_kernel(int dtype, int head_dim, int rows, int cache_mode, bool masked) {
+    const int rpb = valu_rows_per_block(rows);
     if (head_dim == 128) {
         switch (dtype) {
-        case F16: return launch_valu_r<F16, 128>(p, rpb, row_blocks, st);
-        case BF16: return launch_valu_r<BF16, 128>(p, rpb, row_blocks, st);
-        default: return launch_valu_r<F32, 128>(p, rpb, row_blocks, st);
+        case F16: return valu_kernel_r<F16, 128>(rpb, cache_mode, masked);
+        case BF16: return valu_kernel_r<BF16, 128>(rpb, cache_mode, masked);
+        default: return valu_kernel_r<F32, 128>(rpb, cache_mode, masked);
         }
     }
     switch (dtype) {
-    case F16: return launch_valu_r<F16, 64>(p, rpb, row_blocks, st);
-    case BF16: return launch_valu_r<BF16, 64>(p, rpb, row_blocks, st);
-    default: return launch_valu_r<F32, 64>(p, rpb, row_blocks, st);
+    case F16: return valu_kernel_r<F16, 64>(rpb, cache_mode, masked);
+    case BF16: return valu_kernel_r<BF16, 64>(rpb, cache_mode, masked);
+    default: return valu_kernel_r<F32, 64>(rpb, cache_mode, masked);
     }
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
+    const int rpb = valu_rows_per_block(p.rows);
+    int row_blocks = (p.rows + rpb - 1) / rpb;
+    const void* k = select_valu_kernel(dtype, head_dim, p.rows, p.cache_mode, p.q_len > 1);
+    DecodeParams pp = p;
+    void* args[] = {&pp, &row_blocks};
+    return hipLaunchKernel(k, dim3(p.n_split, p.num_kv_heads, p.batch * row_blocks),
+                           dim3(VALU_THREADS), args, 0, st);
 }
 
 }  // namespace kvattn

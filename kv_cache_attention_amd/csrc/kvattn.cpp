@@ -23,12 +23,13 @@ int fail(int code, const std::string& msg) {
     return code;
 }
 
-// Split-KV decomposition: about 8 workgroups per compute unit (256 CUs) for the
-// vector-ALU kernel, with at least 256 attended positions per split; the
-// matrix-core kernel holds one or two workgroups per CU and wants longer splits.
-constexpr int kTargetWorkgroups = 2048;
+// Split-KV decomposition: as many work items as the GPU holds resident at once
+// (the kernel instance's occupancy x compute units), so the whole step runs in one
+// round with no tail, each split at least kMinSplitLen positions.  The workspace
+// is sized for the largest target any kernel instance could ask for (8 per CU on
+// 256 CUs).
+constexpr int kMaxResidentWorkgroups = 2048;
 constexpr int kMinSplitLen = 256;
-constexpr int kTargetWorkgroupsMfma = 512;
 constexpr int kMinSplitLenMfma = 512;
 constexpr int kSplitQuantum = 64;
 constexpr int kMaxSplits = 1024;
@@ -49,6 +50,8 @@ int ilog2(int x) {
 struct kvattn_handle {
     kvattn_config cfg;
     int device;
+    int num_cus;
+    int resident[65];       // per q_len: workgroups of its kernel instance resident at once
     hipStream_t stream;
     int32_t batch;
     int32_t forced_split_len;
@@ -85,12 +88,13 @@ int row_blocks_of(const kvattn_config& c, int q_len) {
     return (rows + rpb - 1) / rpb;
 }
 
-// Automatic split count for `batch` sequences of up to n_att attended positions.
-void auto_plan(const kvattn_config& c, int batch, int q_len, int64_t n_att, int* n_split,
-               int* split_len) {
+// Automatic split count for `batch` sequences of up to n_att attended positions,
+// aiming at `target` resident workgroups.
+void auto_plan(const kvattn_config& c, int batch, int q_len, int64_t n_att, int target,
+               int* n_split, int* split_len) {
     const bool mfma = use_mfma(c, q_len);
     const int64_t units = (int64_t)(batch > 0 ? batch : 1) * c.num_kv_heads * row_blocks_of(c, q_len);
-    int ns = ceil_div(mfma ? kTargetWorkgroupsMfma : kTargetWorkgroups, units);
+    int ns = ceil_div(target, units);
     const int ns_cap = ceil_div(n_att > 0 ? n_att : 1, mfma ? kMinSplitLenMfma : kMinSplitLen);
     if (ns > ns_cap) ns = ns_cap;
     if (ns < 1) ns = 1;
@@ -108,7 +112,7 @@ int64_t workspace_rows(const kvattn_config& c) {
     for (int ql = 1; ql <= c.max_q_len; ++ql) {
         for (int b = 1; b <= c.max_batch; ++b) {
             int ns, len;
-            auto_plan(c, b, ql, c.capacity, &ns, &len);
+            auto_plan(c, b, ql, c.capacity, kMaxResidentWorkgroups, &ns, &len);
             const int64_t rows = (int64_t)b * ql * c.num_q_heads * ns;
             if (rows > best) best = rows;
         }
@@ -187,7 +191,27 @@ int validate_decode_args(const kvattn_handle* h, int32_t q_len, int32_t mask_mod
     return KVATTN_OK;
 }
 
-int plan_for(const kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
+// Workgroups of the kernel instance a decode with q_len would launch that fit on
+// the device at once (occupancy query, cached per q_len).
+int resident_workgroups(kvattn_handle* h, int q_len) {
+    int& r = h->resident[q_len];
+    if (r > 0) return r;
+    const kvattn_config& c = h->cfg;
+    const int rows = rows_of(c, q_len);
+    const bool mfma = use_mfma(c, q_len);
+    const void* k = mfma ? kvattn::select_mfma_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
+                         : kvattn::select_valu_kernel(c.dtype, c.head_dim, rows, c.cache_mode,
+                                                      q_len > 1);
+    int per_cu = 0;
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                  &per_cu, k, mfma ? kvattn::kMfmaThreads : kvattn::kValuThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    r = std::min(per_cu * h->num_cus, kMaxResidentWorkgroups);
+    return r;
+}
+
+int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
              int32_t window, int* n_split, int* split_len) {
     const kvattn_config& c = h->cfg;
     const int64_t n_att = max_attended(c, q_len, mask_mode, n_sink, window);
@@ -195,7 +219,7 @@ int plan_for(const kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n
         *split_len = h->forced_split_len;
         *n_split = ceil_div(n_att > 0 ? n_att : 1, h->forced_split_len);
     } else {
-        auto_plan(c, h->batch, q_len, n_att, n_split, split_len);
+        auto_plan(c, h->batch, q_len, n_att, resident_workgroups(h, q_len), n_split, split_len);
     }
     if (*n_split > 1) {
         const int64_t need = (int64_t)h->batch * q_len * c.num_q_heads * *n_split;
@@ -241,10 +265,13 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
     }
     h->stride_seq = unit * H * D;
     hipError_t e = hipGetDevice(&h->device);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess) {
         delete h;
         return fail(KVATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     }
+    for (int& r : h->resident) r = 0;
     h->ws_rows = workspace_rows(*cfg);
     h->n_units = counter_units(*cfg);
     // the merge addresses partials with 32-bit byte offsets
@@ -298,7 +325,7 @@ int kvattn_set_split_len(kvattn_handle* h, int32_t split_len) {
     return KVATTN_OK;
 }
 
-int kvattn_plan(const kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
+int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
                 int32_t window, int32_t* n_split, int32_t* split_len, int32_t* kernel) {
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
     int rc = validate_decode_args(h, q_len, mask_mode, n_sink, window);
