@@ -32,6 +32,34 @@ from kv_cache_attention_amd import binding as kb  # noqa: E402
 METRIC = "decode-attention effective HBM GB/s (% of MI355X peak) and µs/step, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+COPY_BYTES = 1 << 30   # plain copy of known size, the yardstick for the traffic counters
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: HBM traffic measured for other sources is not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, layout: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    import json as _json
+    path = os.path.join(PROFILES, f"traffic_{workload}_{layout}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = _json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def parse():
@@ -175,7 +203,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(case.name, a.layout),
             "bytes_per_step": step_bytes,
             "flops_per_step": step_flops,
             "event_us_mean": round(ev_mean * 1e3, 2),
@@ -184,6 +212,15 @@ def main():
                      "HIP events on the library's stream",
         },
     }
+    # yardstick for the memory counters: one plain device copy of known size
+    # (outside the timed region; a profiler run scales FETCH/WRITE_SIZE by it)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    rec["config"]["kernel_source_hash"] = kernel_source_hash()
     if not a.no_cpu_baseline:
         rows = a.cpu_rows or default_cpu_rows(case)
         rec["cpu_baseline"] = cpu_baseline(case, d, out_for_copy0(h, d, kcs, vcs, case, mask),
