@@ -164,9 +164,9 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
     // the merge costs a few memory latencies, not one per split.
     constexpr int E4 = NROWS * D / 4;
     constexpr int SG = E4 >= THREADS ? 1 : THREADS / E4;
-    constexpr int EPT = E4 >= THREADS ? E4 / THREADS : 1;
+    constexpr int EPT = E4 >= THREADS ? (E4 + THREADS - 1) / THREADS : 1;
     constexpr int US = 4;  // splits per step
-    static_assert(E4 >= THREADS ? E4 % THREADS == 0 : THREADS % E4 == 0, "shape");
+    static_assert(E4 >= THREADS || THREADS % E4 == 0, "shape");
     const int sg = E4 >= THREADS ? 0 : tid / E4;
     int e4[EPT], r[EPT];
     bool live[EPT];
@@ -175,9 +175,11 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
     float4 a[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        e4[k] = E4 >= THREADS ? tid + k * THREADS : tid % E4;
+        const int e = E4 >= THREADS ? tid + k * THREADS : tid % E4;
+        const bool in = e < E4;  // chunks past the last one (E4 not a multiple of THREADS)
+        e4[k] = in ? e : 0;
         r[k] = e4[k] / (D / 4);
-        live[k] = row0 + r[k] < p.rows;
+        live[k] = in && row0 + r[k] < p.rows;
         part0[k] = live[k] ? row_id_of(p, b, kvh, row0 + r[k]) * n_split : 0;
         mu[k] = live[k] ? sm.M[r[k]] : 0.0f;
         a[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
