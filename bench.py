@@ -154,6 +154,7 @@ def main():
     t0 = time.perf_counter()
     for s in range(a.steps):
         step(s % copies)
+    t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
@@ -181,6 +182,7 @@ def main():
         "warmup": a.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "host_enqueue_us_per_step": round(t_enq * 1e6 / a.steps, 2),
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",

@@ -100,7 +100,18 @@ typedef struct kvattn_config {
     int32_t num_blocks;     /* PAGED: blocks in the pool; otherwise ignored */
     int32_t layout;         /* kvattn_layout */
     float scale;            /* 0 => 1 / sqrt(head_dim) */
+    uint32_t flags;         /* KVATTN_FLAG_* bits, 0 for the defaults */
 } kvattn_config;
+
+/* Flags.
+ * KVATTN_FLAG_DETERMINISTIC: every decode with the same inputs returns the same
+ *   bits.  By default the waves of a workgroup take tiles of positions from a
+ *   shared queue, so the order in which partial sums are added (and with it the
+ *   last bits of the result) depends on timing; with this flag each wave takes a
+ *   fixed set of tiles, at some cost in speed when memory bandwidth is shared
+ *   unevenly.  The result then depends only on the logical positions, not on
+ *   where a paged cache keeps them. */
+#define KVATTN_FLAG_DETERMINISTIC 1u
 
 typedef struct kvattn_handle kvattn_handle;
 

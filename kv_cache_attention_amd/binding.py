@@ -33,7 +33,10 @@ class kvattn_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "dtype", "num_q_heads", "num_kv_heads", "head_dim", "max_batch", "max_q_len",
         "cache_mode", "capacity", "block_size", "num_blocks", "layout")] + [
-        ("scale", ctypes.c_float)]
+        ("scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+FLAG_DETERMINISTIC = 1
 
 
 class KVAttnError(RuntimeError):
@@ -98,10 +101,10 @@ def _dev_ptr(t: Optional[torch.Tensor], name: str):
 def make_config(*, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
                 max_batch: int, max_q_len: int, cache_mode: str, capacity: int,
                 block_size: int = 16, num_blocks: int = 0, layout: str = "token_major",
-                scale: float = 0.0) -> kvattn_config:
+                scale: float = 0.0, deterministic: bool = False) -> kvattn_config:
     return kvattn_config(DTYPE[dtype], num_q_heads, num_kv_heads, head_dim, max_batch, max_q_len,
                          CACHE[cache_mode], capacity, block_size, num_blocks, LAYOUT[layout],
-                         scale)
+                         scale, FLAG_DETERMINISTIC if deterministic else 0)
 
 
 # ------------------------------------------------------------ same names as the C ABI
@@ -170,22 +173,24 @@ class KVAttn:
     def __init__(self, *, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  max_batch: int, max_q_len: int, cache_mode: str, capacity: int,
                  block_size: int = 16, num_blocks: int = 0, layout: str = "token_major",
-                 scale: float = 0.0):
+                 scale: float = 0.0, deterministic: bool = False):
         self.cfg = make_config(dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                                head_dim=head_dim, max_batch=max_batch, max_q_len=max_q_len,
                                cache_mode=cache_mode, capacity=capacity, block_size=block_size,
-                               num_blocks=num_blocks, layout=layout, scale=scale)
+                               num_blocks=num_blocks, layout=layout, scale=scale,
+                               deterministic=deterministic)
         self.dtype = dtype
         self.h = kvattn_create(self.cfg)
 
     @classmethod
     def for_case(cls, case, layout: str = "token_major", max_batch: Optional[int] = None,
-                 max_q_len: Optional[int] = None) -> "KVAttn":
+                 max_q_len: Optional[int] = None, deterministic: bool = False) -> "KVAttn":
         return cls(dtype=case.dtype, num_q_heads=case.num_q_heads,
                    num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
                    max_batch=max_batch or case.batch, max_q_len=max_q_len or case.q_len,
                    cache_mode=case.cache_mode, capacity=case.capacity,
-                   block_size=case.block_size, num_blocks=case.num_blocks, layout=layout)
+                   block_size=case.block_size, num_blocks=case.num_blocks, layout=layout,
+                   deterministic=deterministic)
 
     def close(self) -> None:
         if self.h:

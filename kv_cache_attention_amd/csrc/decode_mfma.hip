@@ -31,6 +31,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "split_merge.hpp"
+#include "work_plan.hpp"
 
 namespace kvattn {
 
@@ -86,9 +87,10 @@ template <int D, int R>
 struct MfmaGeo {
     static constexpr int KS = D / 32;          // k-steps of 32 along d (Q K^T)
     static constexpr int DT16 = D / 16;        // 16-wide d tiles of the output
-    static constexpr int VROW = D * 2 + 16;    // LDS bytes per staged V row: 16-byte aligned,
-                                               // 4 dwords of padding keep reads and writes
-                                               // free of bank conflicts
+    static constexpr int VROW = D * 2 + 32;    // LDS bytes per staged V row: D/2 + 8 dwords,
+                                               // an odd multiple of 8 banks for D = 64, 128,
+                                               // so the 8 rows one transposed read touches
+                                               // per half-wave fall on distinct banks
     static constexpr int VBUF = TILE * VROW;   // LDS bytes per wave
     static constexpr int CPR = D * 2 / 16;     // 16-byte chunks per V row
     static constexpr int PPI = 64 / CPR;       // V rows per wave-wide load
@@ -96,8 +98,13 @@ struct MfmaGeo {
     static constexpr int QFRAGS = R * KS;      // Q^T operand fragments (64 lanes x 16 bytes)
 };
 
+// Workgroups per CU the register budget is cut for (row tiles <= 3).
+#ifndef KVATTN_MFMA_WG_PER_CU
+#define KVATTN_MFMA_WG_PER_CU 1
+#endif
+
 template <int DT, int D, int R, int CACHE>
-__global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? 2 : 1) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) void decode_mfma_kernel(const DecodeParams p) {
     using G = MfmaGeo<D, R>;
     constexpr int KS = G::KS, DT16 = G::DT16, VROW = G::VROW, CPR = G::CPR, PPI = G::PPI,
                   NV = G::NV;
@@ -113,20 +120,24 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? 2 : 1) void decode_mfma_kern
     __shared__ float sm_m[MFMA_WAVES][NQ];
     __shared__ float sm_l[MFMA_WAVES][NQ];
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
-    const SeqSpan s = seq_span(p, b);
-    const int nvalid = valid_splits(p, s);
-    if (split >= nvalid) return;
-    const int32_t j0 = split * p.split_len;
-    const int32_t j1 = min(j0 + p.split_len, s.count);
+    __shared__ float sm_f[MFMA_WAVES][NQ];
+    __shared__ float sm_M[NQ], sm_L[NQ];
+
+    const int wg = blockIdx.x;
+    const int n_wg = gridDim.x;
+    const WgRange range = plan_range<MFMA_THREADS>(p, wg, n_wg);
 
     const int tid = threadIdx.x;
     const int wave = tid / 64;
     const int l = tid % 64;
     const int lr = l % 16;  // operand row / output column
     const int lq = l / 16;  // operand k-group / output row group
+
+    for_each_piece(p, range, wg, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
+    const int b = pc.b;
+    const int kvh = pc.seg;
+    const int32_t j0 = pc.ja;
+    const int32_t j1 = pc.jb;
 
     // rows' new-token index (for the causal / window mask); padding rows act as the last
     int row_i[R];
@@ -330,24 +341,25 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? 2 : 1) void decode_mfma_kern
                 for (int qt = 0; qt < R; ++qt) o[dt][qt] *= alpha[qt];
         }
 
-        // O^T += V^T . P^T, V^T read back transposed from LDS with the same position
-        // permutation as P^T
+        // O^T += V^T . P^T.  V^T comes back from LDS with the gfx950 transposed read
+        // (ds_read_b64_tr_b16): within each 16-lane group, lane j receives element j%4
+        // of the rows that lanes j/4, j/4 + 4, j/4 + 8, j/4 + 12 address.  Lane i of
+        // group g addresses the 4 d values dt*16 + 4*(i%4) .. +3 of position
+        // 4g + i/4 (+16 for the second half), so lane j gets d = dt*16 + j at positions
+        // 4g .. 4g + 3 (and 16 + 4g ..): the A operand in the P^T position order.
         __builtin_amdgcn_wave_barrier();
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef s16x4 __attribute__((address_space(3))) * lds_s16x4;
+        const uint32_t vrow0 = (uint32_t)(size_t)vbuf + (lq * 4 + lr / 4) * VROW + (lr % 4) * 8;
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {
-            const char* col = vbuf + (dt * 16 + lr) * 2;
-            uint32_t w[4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const char* r0 = col + (h * 16 + lq * 4) * VROW;
-                const uint32_t a0 = *reinterpret_cast<const uint16_t*>(r0);
-                const uint32_t a1 = *reinterpret_cast<const uint16_t*>(r0 + VROW);
-                const uint32_t a2 = *reinterpret_cast<const uint16_t*>(r0 + 2 * VROW);
-                const uint32_t a3 = *reinterpret_cast<const uint16_t*>(r0 + 3 * VROW);
-                w[2 * h] = a0 | (a1 << 16);
-                w[2 * h + 1] = a2 | (a3 << 16);
-            }
-            const u32x4 va = {w[0], w[1], w[2], w[3]};
+            const uint32_t a0 = vrow0 + dt * 32;
+            const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(size_t)a0);
+            const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(size_t)(a0 + 16 * VROW));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, h0);
+            const u32x2 w1 = __builtin_bit_cast(u32x2, h1);
+            const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
 #pragma unroll
             for (int qt = 0; qt < R; ++qt) {
                 const u32x4 pb = {pf[qt][0], pf[qt][1], pf[qt][2], pf[qt][3]};
@@ -369,8 +381,6 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? 2 : 1) void decode_mfma_kern
     }
     __syncthreads();  // also: every wave is done with its V staging area
     // per row: the workgroup's max M and sum L, and each wave's factor 2^(m_w - M)
-    __shared__ float sm_f[MFMA_WAVES][NQ];
-    __shared__ float sm_M[NQ], sm_L[NQ];
     if (tid < NQ) {
         float M = NEG_INF;
 #pragma unroll
@@ -415,25 +425,27 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? 2 : 1) void decode_mfma_kern
         if (n >= p.rows) continue;
         const float4 A = *reinterpret_cast<const float4*>(osum + n * D + d);
         const int64_t rid = row_id_of(p, b, kvh, n);
-        if (nvalid == 1) {
+        if (pc.nparts == 1) {
             const float L = sm_L[n];
             const float inv = L > 0.0f ? 1.0f / L : 0.0f;
             const uint2 w = {pack2<DT>(A.x * inv, A.y * inv), pack2<DT>(A.z * inv, A.w * inv)};
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
         } else {
-            const int64_t part = rid * p.n_split + split;
+            const int64_t part = (pc.slot0 + pc.part) * NQ + n;
             store_partial4(p, part * D + d, A);
             if (d == 0) store_partial_ml(p, part, sm_M[n], sm_L[n]);
         }
     }
-    if (nvalid > 1) {
-        // the staging area is free again: the merge's scratch lives there
-        static_assert(sizeof(MergeSmem<NQ, MFMA_THREADS>) <= SMEM_V, "merge scratch");
-        __syncthreads();
+    // the staging area is free again: the merge's scratch lives there
+    static_assert(sizeof(MergeSmem<NQ, MFMA_THREADS>) <= SMEM_V, "merge scratch");
+    __syncthreads();
+    if (pc.nparts > 1) {
         auto& msm = *reinterpret_cast<MergeSmem<NQ, MFMA_THREADS>*>(smem);
-        arrive_and_merge<DT, D, NQ, MFMA_THREADS>(p, b, kvh, 0, b * p.num_kv_heads + kvh, nvalid,
-                                                  msm);
+        arrive_and_merge<DT, D, NQ, MFMA_THREADS>(p, b, kvh, 0, pc.unit, pc.slot0, pc.nparts, msm);
+        __syncthreads();  // LDS is reused by the next piece
     }
+    });
+    zero_empty_sequences<DT, MFMA_THREADS, D>(p, wg, n_wg);
 }
 
 bool mfma_supported(int dtype, int head_dim, int rows) {
@@ -469,13 +481,13 @@ const void* select_mfma_kernel(int dtype, int head_dim, int rows, int cache_mode
                            : mfma_kernel_r<BF16, 64>(rows, cache_mode);
 }
 
-hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,
+                              hipStream_t st) {
     const void* k = select_mfma_kernel(dtype, head_dim, p.rows, p.cache_mode);
     if (!k) return hipErrorInvalidValue;
     DecodeParams pp = p;
     void* args[] = {&pp};
-    return hipLaunchKernel(k, dim3(p.n_split, p.num_kv_heads, p.batch), dim3(MFMA_THREADS), args,
-                           0, st);
+    return hipLaunchKernel(k, dim3(grid), dim3(MFMA_THREADS), args, 0, st);
 }
 
 }  // namespace kvattn

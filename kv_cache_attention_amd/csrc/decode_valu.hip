@@ -1,32 +1,38 @@
 // Split-KV flash-decoding on the vector ALUs, for up to 16 query rows per KV head.
 //
-// One workgroup (256 lanes = 4 wave64) owns one (sequence, KV head, split): a
-// run of split_len attended positions.  Each position's K row (and V row) of
-// head_dim elements is read by one "lane group" of head_dim*bytes/16 lanes with
-// one 16-byte load per lane, so a wave instruction covers whole 256-byte rows and
-// every byte of K and V is loaded exactly once, straight into registers (each
-// byte feeds exactly one lane, so staging it through LDS would add a write and a
-// read with no reuse).  All query rows that share the KV head (the GQA group
-// times the q_len new tokens) live in every lane, so one K/V fetch serves the
-// whole group.
+// One workgroup per compute unit streams one equal slice of the step's work (the
+// balanced decomposition of work_plan.hpp): a run of attended positions of one
+// or more (sequence, KV head, row block) segments.  Each position's K row (and
+// V row) of head_dim elements is read by one "lane group" of head_dim*bytes/16
+// lanes with one 16-byte load per lane, so a wave instruction covers whole
+// 256-byte rows and every byte of K and V is loaded exactly once, straight into
+// registers (each byte feeds exactly one lane, so staging it through LDS would
+// add a write and a read with no reuse).  All query rows that share the KV head
+// (the GQA group times the q_len new tokens) live in every lane, so one K/V
+// fetch serves the whole group.
 //
-// Per tile of U positions a lane group forms the scores with packed dot
+// Within a piece the waves take wave tiles (U positions per lane group) from a
+// counter in LDS, so a wave that the memory system serves faster takes more
+// tiles and the compute unit finishes at its average pace rather than at its
+// slowest wave's.  Per tile a lane group forms the scores with packed dot
 // products, sums them over its lanes with DPP, and folds them into its own
 // running (max, sum, accumulator) - the online softmax of the Flash Attention
 // section of the nextadmin.net lesson "KV cache and Flash Attention" (running
 // max and sum across tiles, rescale the old terms by exp(m_old - m_new), which
 // is 0 when nothing was seen yet).  Scores are kept in the exp2 domain
-// (scale * log2 e folded into one multiply).  At the end the lane groups of a
-// wave merge through cross-lane shuffles, the four waves through LDS, and the
-// workgroup writes either the final rows (its sequence needs one split) or its
-// unnormalised partial (acc, m, l); the last workgroup of the (sequence, KV
-// head) to finish merges the partials (split_merge.hpp).
+// (scale * log2 e folded into one multiply).  At the end of a piece the lane
+// groups of a wave merge through cross-lane shuffles, the waves through LDS, and
+// the workgroup writes either the final rows (the piece is a whole segment) or
+// its unnormalised partial (acc, m, l); the last piece of a segment to finish
+// merges the partials (split_merge.hpp).
 //
-// Paged caches: the page-table entries of the next tile are read while the
-// current tile is processed, so the K/V loads never wait on a table read.
+// Loads are rolling: a wave issues the next tile's K as soon as the current
+// tile's scores have consumed K, and its V as soon as the current V is
+// accumulated, so every wave has loads in flight while it computes.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "split_merge.hpp"
+#include "work_plan.hpp"
 
 namespace kvattn {
 
@@ -39,7 +45,6 @@ struct Geo {
     static constexpr int LPR = D / EPL;   // lanes per (position, head) row
 };
 
-constexpr int VALU_THREADS = 256;
 
 __device__ __forceinline__ u32x4 load16(const void* base, int64_t elem_off, int eb) {
     return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + elem_off * eb);
@@ -92,231 +97,288 @@ __device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
 // MASKED: q_len > 1, so rows of one sequence attend different position sets and
 // every score gets its row's causal / window test (with one new row the attended
 // union is exactly that row's set and no per-row test is needed).
-template <int DT, int D, int ROWS, int CACHE, int U, bool MASKED>
-__global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeParams p,
-                                                                   int row_blocks) {
+template <int DT, int D, int ROWS, int CACHE, int U, bool MASKED, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const DecodeParams p) {
     using G = Geo<DT, D>;
     constexpr int EPL = G::EPL, LPR = G::LPR, EB = G::EB;
-    constexpr int NLG = VALU_THREADS / LPR;  // lane groups per workgroup
+    constexpr int THREADS = NWAVES * 64;
+    constexpr int LGW = 64 / LPR;          // lane groups per wave
+    constexpr int32_t TWW = LGW * U;       // positions per wave tile
     constexpr float NEG_INF = -__builtin_inff();
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z / row_blocks;
-    const int rb = blockIdx.z - b * row_blocks;
-
-    const SeqSpan s = seq_span(p, b);
-    const int nvalid = valid_splits(p, s);
-    if (split >= nvalid) return;
-    const int32_t j0 = split * p.split_len;
-    const int32_t j1 = min(j0 + p.split_len, s.count);
+    const int wg = blockIdx.x;
+    const int n_wg = gridDim.x;
+    const WgRange range = plan_range<THREADS>(p, wg, n_wg);
 
     const int tid = threadIdx.x;
-    const int lane = tid % LPR;
-    const int lg = tid / LPR;
-    const int d0 = lane * EPL;
-
-    // Query rows of this KV head: row r = i * group + hg  (new token i, head kvh*group+hg)
-    u32x4 qv[ROWS];
-    int row_i[ROWS];
-    int64_t row_id[ROWS];  // index of the row in out's [batch, q_len, Hq] order
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        const int rg = rb * ROWS + r;
-        const bool ok = rg < p.rows;
-        const int i = ok ? rg / p.group : 0;
-        const int h = kvh * p.group + (ok ? rg - i * p.group : 0);
-        row_i[r] = ok ? i : -1;
-        row_id[r] = ((int64_t)b * p.q_len + i) * p.num_q_heads + h;
-        qv[r] = ok ? load16(p.q, row_id[r] * D + d0, EB) : u32x4{0, 0, 0, 0};
-    }
-
-    float m[ROWS], l[ROWS], acc[ROWS][EPL];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        m[r] = NEG_INF;
-        l[r] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[r][e] = 0.0f;
-    }
-    // per-row bounds for MASKED: row r attends pos iff pos <= hi[r] and
-    // (pos < n_sink or pos >= lo[r])  (lo = 0 for the causal mask)
-    int32_t hi[ROWS], lo[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        const int32_t P = s.T - p.q_len + (row_i[r] >= 0 ? row_i[r] : p.q_len - 1);
-        hi[r] = P;
-        lo[r] = p.mask_mode == MASK_SINK_WINDOW ? P - p.window + 1 : 0;
-    }
-
-    // Loads are branch-free: a lane whose position lies past the split (or behind a
-    // page-table entry outside the pool) loads a clamped, valid address and its
-    // data is discarded by selects (score -> -inf, V -> 0), never multiplied in.
-    // Paged caches read the page-table entries one tile ahead of use.
-    constexpr int32_t TW = NLG * U;  // positions per workgroup tile
-    int32_t blk[U];
-    auto pages = [&](int32_t base) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t j = min(base + u * NLG + lg, j1 - 1);
-            blk[u] = page_entry(p, b, span_pos(s, j));
-        }
-    };
-    if constexpr (CACHE == PAGED) pages(j0);
-
-    for (int32_t base = j0; base < j1; base += TW) {
-        u32x4 kw[U], vw[U];
-        int32_t pos[U];
-        bool val[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t j = base + u * NLG + lg;
-            val[u] = j < j1;
-            pos[u] = span_pos(s, min(j, j1 - 1));
-            Loc L;
-            if constexpr (CACHE == PAGED) {
-                L = paged_loc(p, blk[u], pos[u]);
-                val[u] = val[u] && L.unit >= 0;
-                L.unit = L.unit >= 0 ? L.unit : 0;
-            } else {
-                L = locate<CACHE>(p, s, b, pos[u]);
-            }
-            const int64_t off = row_offset(p, L, kvh) + d0;
-            kw[u] = load16(p.k, off, EB);
-            vw[u] = load16(p.v, off, EB);
-        }
-        if constexpr (CACHE == PAGED) pages(base + TW);
-        // raw scores q.k; the softmax scale (times log2 e) is applied inside the
-        // exp2 argument, so the running max m is kept in scaled units
-        float sc[ROWS][U];
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float x = group_sum<LPR>(dot16<DT>(qv[r], kw[u]));
-                bool ok = val[u];
-                if constexpr (MASKED)
-                    ok = ok & (pos[u] <= hi[r]) & ((pos[u] < p.n_sink) | (pos[u] >= lo[r]));
-                sc[r][u] = ok ? x : NEG_INF;
-            }
-        }
-        float vf[U][EPL];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            unpack16<DT>(vw[u], vf[u]);
-            // a paged position behind an out-of-pool entry was read from block 0 and
-            // may hold anything; every other discarded lane read an attended position
-            if constexpr (CACHE == PAGED) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) vf[u][e] = val[u] ? vf[u][e] : 0.0f;
-            }
-        }
-        const float c = p.scale_log2;
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            float mt = sc[r][0];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[r][u]);
-            const float m_new = fmaxf(m[r], mt * c);  // c > 0: max commutes with the scale
-            const float m_use = m_new == NEG_INF ? 0.0f : m_new;
-            if (__any(m_new != m[r])) {  // rescale only when some lane's max moved
-                const float alpha = fast_exp2(m[r] - m_use);  // 0 while nothing was seen
-                l[r] *= alpha;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[r][e] *= alpha;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float pw = fast_exp2(fmaf(sc[r][u], c, -m_use));
-                l[r] += pw;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(pw, vf[u][e], acc[r][e]);
-            }
-            m[r] = m_new;
-        }
-    }
-
-    // Merge the lane groups of each wave (butterfly over lane offsets LPR .. 32).
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            const float mo = __shfl_xor(m[r], off, 64);
-            const float lo = __shfl_xor(l[r], off, 64);
-            const float M = fmaxf(m[r], mo);
-            const float Mu = M == NEG_INF ? 0.0f : M;
-            const float a = fast_exp2(m[r] - Mu);
-            const float c = fast_exp2(mo - Mu);
-            l[r] = l[r] * a + lo * c;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float ao = __shfl_xor(acc[r][e], off, 64);
-                acc[r][e] = acc[r][e] * a + ao * c;
-            }
-            m[r] = M;
-        }
-    }
-
-    // Merge the four waves through LDS.
-    constexpr int NW = VALU_THREADS / 64;
-    __shared__ float sm_acc[NW][ROWS][D];
-    __shared__ float sm_ml[NW][ROWS][2];
     const int wave = tid / 64;
     const int lw = tid % 64;
-    if (lw < LPR) {
+    const int lane = lw % LPR;
+    const int lgw = lw / LPR;  // lane group within the wave
+    const int d0 = lane * EPL;
+
+    __shared__ float sm_acc[NWAVES][ROWS][D];
+    __shared__ float sm_ml[NWAVES][ROWS][2];
+    __shared__ MergeSmem<ROWS, THREADS> msm;
+    __shared__ int s_next_tile;
+
+    // Byte addresses: K row of (unit, slot idx) at kb + unit * unit_bytes + idx * tok_bytes
+    // (unit = the pool block for paged caches, folded into kb otherwise); V at K + dv.
+    const uint32_t tok_bytes = (uint32_t)(p.stride_tok * EB);
+    const uint32_t unit_bytes = (uint32_t)(p.stride_seq * EB);
+    const int64_t dv = reinterpret_cast<const char*>(p.v) - reinterpret_cast<const char*>(p.k);
+    const float c = p.scale_log2;
+
+    for_each_piece(p, range, wg, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
+        const int b = pc.b;
+        const int kvh = pc.seg / p.row_blocks;
+        const int rb = pc.seg - kvh * p.row_blocks;
+        const int32_t n_tiles = (pc.jb - pc.ja + TWW - 1) / TWW;
+        if (tid == 0) s_next_tile = NWAVES;  // wave w starts with tile w
+        __syncthreads();
+
+        // Query rows of this KV head: row r = i * group + hg (new token i, head kvh*group+hg)
+        u32x4 qv[ROWS];
+        int row_i[ROWS];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
+            const int rg = rb * ROWS + r;
+            const bool ok = rg < p.rows;
+            const int i = ok ? rg / p.group : 0;
+            const int h = kvh * p.group + (ok ? rg - i * p.group : 0);
+            row_i[r] = ok ? i : -1;
+            const int64_t rid = ((int64_t)b * p.q_len + i) * p.num_q_heads + h;
+            qv[r] = ok ? load16(p.q, rid * D + d0, EB) : u32x4{0, 0, 0, 0};
+        }
+        // MASKED: row r attends pos iff pos <= hi[r] and (pos < n_sink or pos >= lo[r])
+        int32_t hi[ROWS], lo[ROWS];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) sm_acc[wave][r][d0 + e] = acc[r][e];
-            if (lw == 0) {
-                sm_ml[wave][r][0] = m[r];
-                sm_ml[wave][r][1] = l[r];
+        for (int r = 0; r < ROWS; ++r) {
+            const int32_t P = s.T - p.q_len + (row_i[r] >= 0 ? row_i[r] : p.q_len - 1);
+            hi[r] = P;
+            lo[r] = p.mask_mode == MASK_SINK_WINDOW ? P - p.window + 1 : 0;
+        }
+        float m[ROWS], l[ROWS], acc[ROWS][EPL];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            m[r] = NEG_INF;
+            l[r] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[r][e] = 0.0f;
+        }
+
+        const char* kb = reinterpret_cast<const char*>(p.k) + ((int64_t)kvh * p.stride_head + d0) * EB;
+        if constexpr (CACHE != PAGED) kb += (int64_t)b * p.stride_seq * EB;
+
+        // Wave tile t covers work indices ja + t * TWW ...: lane group g of the wave
+        // takes ja + t * TWW + u * LGW + g (u < U), so each load instruction reads LGW
+        // consecutive positions.  Loads are branch-free: a lane past the piece (or
+        // behind a page-table entry outside the pool) loads a clamped, valid address
+        // and its data is discarded by selects (score -> -inf, V -> 0).
+        int32_t pos[U];
+        bool val[U];
+        const char* ka[U];
+        int32_t blk[U];  // paged: page-table entries of the tile to address next
+        auto fetch_pages = [&](int32_t t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t j = min(pc.ja + t * TWW + u * LGW + lgw, pc.jb - 1);
+                blk[u] = page_entry(p, b, span_pos(s, j));
+            }
+        };
+        auto address = [&](int32_t t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t j = pc.ja + t * TWW + u * LGW + lgw;
+                val[u] = j < pc.jb;
+                pos[u] = span_pos(s, min(j, pc.jb - 1));
+                if constexpr (CACHE == PAGED) {
+                    const bool in_pool = (uint32_t)blk[u] < (uint32_t)p.num_blocks;
+                    val[u] = val[u] && in_pool;
+                    const uint32_t unit = in_pool ? (uint32_t)blk[u] : 0u;
+                    const uint32_t idx = (uint32_t)pos[u] & ((1u << p.log2_block) - 1);
+                    ka[u] = kb + (uint64_t)unit * unit_bytes + idx * tok_bytes;
+                } else {
+                    const Loc L = locate<CACHE>(p, s, b, pos[u]);
+                    ka[u] = kb + (uint64_t)(uint32_t)L.idx * tok_bytes;
+                }
+            }
+        };
+        int32_t cur = wave;
+        // next tile for this wave: one LDS atomic per tile, issued a tile ahead
+        // (deterministic mode: every NWAVES-th tile, a fixed summation order)
+        auto grab = [&]() __attribute__((always_inline)) -> int32_t {
+            if (p.deterministic) return cur + NWAVES;
+            int32_t t = 0;
+            if (lw == 0)
+                t = __hip_atomic_fetch_add(&s_next_tile, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            return __builtin_amdgcn_readfirstlane(t);
+        };
+
+        u32x4 kw[U], vw[U];
+        if (cur < n_tiles) {
+            if constexpr (CACHE == PAGED) fetch_pages(cur);
+            address(cur);
+#pragma unroll
+            for (int u = 0; u < U; ++u) kw[u] = *reinterpret_cast<const u32x4*>(ka[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) vw[u] = *reinterpret_cast<const u32x4*>(ka[u] + dv);
+        }
+        int32_t nxt = cur < n_tiles ? grab() : n_tiles;
+        if constexpr (CACHE == PAGED) {
+            if (nxt < n_tiles) fetch_pages(nxt);
+        }
+        while (cur < n_tiles) {
+            const bool more = nxt < n_tiles;
+            // raw scores q.k; the softmax scale (times log2 e) is applied inside the
+            // exp2 argument, so the running max m is kept in scaled units
+            float sc[ROWS][U];
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float x = group_sum<LPR>(dot16<DT>(qv[r], kw[u]));
+                    bool ok = val[u];
+                    if constexpr (MASKED)
+                        ok = ok & (pos[u] <= hi[r]) & ((pos[u] < p.n_sink) | (pos[u] >= lo[r]));
+                    sc[r][u] = ok ? x : NEG_INF;
+                }
+            }
+            // a paged position behind an out-of-pool entry was read from block 0 and
+            // may hold anything; every other discarded lane read an attended position
+            bool vok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) vok[u] = val[u];
+            if (more) {
+                address(nxt);
+#pragma unroll
+                for (int u = 0; u < U; ++u) kw[u] = *reinterpret_cast<const u32x4*>(ka[u]);
+            }
+            float pw[ROWS][U];
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+                float mt = sc[r][0];
+#pragma unroll
+                for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[r][u]);
+                const float m_new = fmaxf(m[r], mt * c);  // c > 0: max commutes with the scale
+                const float m_use = m_new == NEG_INF ? 0.0f : m_new;
+                if (__any(m_new != m[r])) {  // rescale only when some lane's max moved
+                    const float alpha = fast_exp2(m[r] - m_use);  // 0 while nothing was seen
+                    l[r] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[r][e] *= alpha;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    pw[r][u] = fast_exp2(fmaf(sc[r][u], c, -m_use));
+                    l[r] += pw[r][u];
+                }
+                m[r] = m_new;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float vf[EPL];
+                unpack16<DT>(vw[u], vf);
+                if constexpr (CACHE == PAGED) {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) vf[e] = vok[u] ? vf[e] : 0.0f;
+                }
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(pw[r][u], vf[e], acc[r][e]);
+            }
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) vw[u] = *reinterpret_cast<const u32x4*>(ka[u] + dv);
+            }
+            cur = nxt;
+            if (cur < n_tiles) {
+                nxt = grab();
+                if constexpr (CACHE == PAGED) {
+                    if (nxt < n_tiles) fetch_pages(nxt);
+                }
             }
         }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < ROWS * D; idx += VALU_THREADS) {
-        const int r = idx / D;
-        const int d = idx - r * D;
-        if (rb * ROWS + r >= p.rows) continue;
-        float M = NEG_INF;
+
+        // Merge the lane groups of each wave (butterfly over lane offsets LPR .. 32).
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][r][0]);
-        const float Mu = M == NEG_INF ? 0.0f : M;
-        float L = 0.0f, A = 0.0f;
+        for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float f = fast_exp2(sm_ml[w][r][0] - Mu);
-            L += sm_ml[w][r][1] * f;
-            A += sm_acc[w][r][d] * f;
-        }
-        const int64_t rid = row_id_of(p, b, kvh, rb * ROWS + r);
-        if (nvalid == 1) {
-            store_elem<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
-        } else {
-            const int64_t part = rid * p.n_split + split;
-            store_partial(p.ws_acc + part * D + d, A);
-            if (d == 0) {
-                store_partial(p.ws_ml + part * 2, M);
-                store_partial(p.ws_ml + part * 2 + 1, L);
+            for (int r = 0; r < ROWS; ++r) {
+                const float mo = __shfl_xor(m[r], off, 64);
+                const float lo2 = __shfl_xor(l[r], off, 64);
+                const float M = fmaxf(m[r], mo);
+                const float Mu = M == NEG_INF ? 0.0f : M;
+                const float a = fast_exp2(m[r] - Mu);
+                const float cc = fast_exp2(mo - Mu);
+                l[r] = l[r] * a + lo2 * cc;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const float ao = __shfl_xor(acc[r][e], off, 64);
+                    acc[r][e] = acc[r][e] * a + ao * cc;
+                }
+                m[r] = M;
             }
         }
-    }
-    if (nvalid > 1) {
-        __shared__ MergeSmem<ROWS, VALU_THREADS> msm;
-        const int unit = (b * p.num_kv_heads + kvh) * row_blocks + rb;
-        arrive_and_merge<DT, D, ROWS, VALU_THREADS>(p, b, kvh, rb * ROWS, unit, nvalid, msm);
-    }
+
+        // Merge the waves through LDS.
+        if (lw < LPR) {
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sm_acc[wave][r][d0 + e] = acc[r][e];
+                if (lw == 0) {
+                    sm_ml[wave][r][0] = m[r];
+                    sm_ml[wave][r][1] = l[r];
+                }
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < ROWS * D; idx += THREADS) {
+            const int r = idx / D;
+            const int d = idx - r * D;
+            if (rb * ROWS + r >= p.rows) continue;
+            float M = NEG_INF;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) M = fmaxf(M, sm_ml[w][r][0]);
+            const float Mu = M == NEG_INF ? 0.0f : M;
+            float L = 0.0f, A = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) {
+                const float f = fast_exp2(sm_ml[w][r][0] - Mu);
+                L += sm_ml[w][r][1] * f;
+                A += sm_acc[w][r][d] * f;
+            }
+            if (pc.nparts == 1) {
+                const int64_t rid = row_id_of(p, b, kvh, rb * ROWS + r);
+                store_elem<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
+            } else {
+                const int64_t part = (pc.slot0 + pc.part) * ROWS + r;
+                store_partial(p.ws_acc + part * D + d, A);
+                if (d == 0) {
+                    store_partial(p.ws_ml + part * 2, M);
+                    store_partial(p.ws_ml + part * 2 + 1, L);
+                }
+            }
+        }
+        if (pc.nparts > 1)
+            arrive_and_merge<DT, D, ROWS, THREADS>(p, b, kvh, rb * ROWS, pc.unit, pc.slot0,
+                                                   pc.nparts, msm);
+        __syncthreads();  // LDS is reused by the next piece
+    });
+    zero_empty_sequences<DT, THREADS, D>(p, wg, n_wg);
 }
 
 // ---------------------------------------------------------------- host launchers
 
 // Positions per lane group per tile.
 #ifndef KVATTN_VALU_U_SMALL
-#define KVATTN_VALU_U_SMALL 8   // 1 or 2 rows
+#define KVATTN_VALU_U_SMALL 4   // 1 or 2 rows
 #endif
 #ifndef KVATTN_VALU_U_MID
-#define KVATTN_VALU_U_MID 8     // 4 rows
+#define KVATTN_VALU_U_MID 4     // 4 rows
 #endif
 #ifndef KVATTN_VALU_U_LARGE
 #define KVATTN_VALU_U_LARGE 4   // 8 or 16 rows
@@ -324,12 +386,20 @@ __global__ __launch_bounds__(VALU_THREADS) void decode_valu_kernel(const DecodeP
 
 // Kernel selection: one instance per (dtype, head_dim, row bucket, cache form,
 // per-row mask); launches and occupancy queries go through the same choice.
+// Waves per workgroup (one workgroup per compute unit): as many as the register
+// budget of the row bucket allows.
+constexpr int valu_waves(int rows_per_block) {
+    return rows_per_block <= 2 ? 12 : (rows_per_block <= 4 ? 8 : 4);
+}
+
 template <int DT, int D, int ROWS, int CACHE>
 static const void* valu_kernel_t(bool masked) {
     constexpr int U = ROWS <= 2 ? KVATTN_VALU_U_SMALL
                                 : (ROWS <= 4 ? KVATTN_VALU_U_MID : KVATTN_VALU_U_LARGE);
-    return masked ? reinterpret_cast<const void*>(&decode_valu_kernel<DT, D, ROWS, CACHE, U, true>)
-                  : reinterpret_cast<const void*>(&decode_valu_kernel<DT, D, ROWS, CACHE, U, false>);
+    constexpr int NW = valu_waves(ROWS);
+    return masked
+               ? reinterpret_cast<const void*>(&decode_valu_kernel<DT, D, ROWS, CACHE, U, true, NW>)
+               : reinterpret_cast<const void*>(&decode_valu_kernel<DT, D, ROWS, CACHE, U, false, NW>);
 }
 
 template <int DT, int D, int ROWS>
@@ -351,6 +421,8 @@ static const void* valu_kernel_r(int rows_per_block, int cache_mode, bool masked
     default: return valu_kernel_c<DT, D, 16>(cache_mode, masked);
     }
 }
+
+int valu_threads(int rows) { return 64 * valu_waves(valu_rows_per_block(rows)); }
 
 int valu_rows_per_block(int rows) {
     if (rows <= 1) return 1;
@@ -376,14 +448,12 @@ const void* select_valu_kernel(int dtype, int head_dim, int rows, int cache_mode
     }
 }
 
-hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t st) {
-    const int rpb = valu_rows_per_block(p.rows);
-    int row_blocks = (p.rows + rpb - 1) / rpb;
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, int grid,
+                              hipStream_t st) {
     const void* k = select_valu_kernel(dtype, head_dim, p.rows, p.cache_mode, p.q_len > 1);
     DecodeParams pp = p;
-    void* args[] = {&pp, &row_blocks};
-    return hipLaunchKernel(k, dim3(p.n_split, p.num_kv_heads, p.batch * row_blocks),
-                           dim3(VALU_THREADS), args, 0, st);
+    void* args[] = {&pp};
+    return hipLaunchKernel(k, dim3(grid), dim3(valu_threads(p.rows)), args, 0, st);
 }
 
 }  // namespace kvattn

@@ -21,16 +21,20 @@ struct DecodeParams {
     const int32_t* block_table;
     const int32_t* seq_lens;
     void* out;
-    float* ws_acc;        // [rows_total, n_split, D]  split partials (unnormalised)
-    float* ws_ml;         // [rows_total, n_split, 2]  (running max m, sum l), log2 domain
-    int32_t* counters;    // [batch, Hkv, row blocks] arrivals per unit, 0 between calls
+    float* ws_acc;        // [slots, seg_rows, D]  partials of split segments (unnormalised)
+    float* ws_ml;         // [slots, seg_rows, 2]  (running max m, sum l), log2 domain
+    int32_t* counters;    // [batch, Hkv, row blocks] arrivals per segment, 0 between calls
     int64_t stride_seq;   // elements: sequence (contiguous/ring) or block (paged)
     int64_t stride_head;  // elements: KV head
     int64_t stride_tok;   // elements: slot within a sequence / block
     int32_t batch, num_q_heads, num_kv_heads, group, q_len, rows;
     int32_t cache_mode, mask_mode, n_sink, window;
     int32_t capacity, log2_block, num_blocks, blocks_per_seq;
-    int32_t n_split, split_len;
+    int32_t row_blocks;   // segments per (sequence, KV head): blocks of query rows
+    int32_t segs_per_seq; // num_kv_heads * row_blocks
+    int32_t seg_rows;     // rows per segment as laid out in the workspace
+    int32_t min_chunk;    // smallest share of work per workgroup (positions)
+    int32_t deterministic;  // waves take fixed tiles instead of a shared queue
     float scale_log2;     // softmax scale * log2(e): scores are kept in the exp2 domain
 };
 
@@ -150,13 +154,6 @@ __device__ __forceinline__ bool row_attends(const DecodeParams& p, const SeqSpan
     if (pos > P) return false;
     if (p.mask_mode == MASK_CAUSAL) return true;
     return pos < p.n_sink || pos >= P - p.window + 1;
-}
-
-// Number of split work items that hold attended positions for a sequence (>= 1:
-// split 0 always runs so that an empty sequence still produces its zero rows).
-__device__ __forceinline__ int32_t valid_splits(const DecodeParams& p, const SeqSpan& s) {
-    const int32_t n = (s.count + p.split_len - 1) / p.split_len;
-    return n < 1 ? 1 : (n > p.n_split ? p.n_split : n);
 }
 
 // ---------------------------------------------------------------- element types

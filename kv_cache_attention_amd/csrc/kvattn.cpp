@@ -23,16 +23,20 @@ int fail(int code, const std::string& msg) {
     return code;
 }
 
-// Split-KV decomposition: as many work items as the GPU holds resident at once
-// (the kernel instance's occupancy x compute units), so the whole step runs in one
-// round with no tail, each split at least kMinSplitLen positions.  The workspace
-// is sized for the largest target any kernel instance could ask for (8 per CU on
-// 256 CUs).
+// Work decomposition: the flat list of (sequence, KV head, row block) segments is
+// cut into equal slices, one per workgroup, with as many workgroups as the GPU
+// holds resident at once for the kernel instance (occupancy x compute units), so
+// the step runs in one round with no tail.  A slice is at least kMinChunk
+// positions (kMinChunkMfma for the matrix-core kernel, whose per-piece epilogue
+// is heavier).  The split points are placed on the device from seq_lens.
+#ifndef KVATTN_GRID_FACTOR
+#define KVATTN_GRID_FACTOR 1
+#endif
 constexpr int kMaxResidentWorkgroups = 2048;
-constexpr int kMinSplitLen = 256;
-constexpr int kMinSplitLenMfma = 512;
-constexpr int kSplitQuantum = 64;
-constexpr int kMaxSplits = 1024;
+constexpr int kGridFactor = KVATTN_GRID_FACTOR;  // workgroups launched per resident slot
+constexpr int kMinChunk = 256;
+constexpr int kMinChunkMfma = 512;
+constexpr int kChunkQuantum = 64;
 constexpr int kMaxQLen = 64;
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -54,10 +58,10 @@ struct kvattn_handle {
     int resident[65];       // per q_len: workgroups of its kernel instance resident at once
     hipStream_t stream;
     int32_t batch;
-    int32_t forced_split_len;
-    float* ws;              // split partials: acc [ws_rows, D], (m, l) [ws_rows, 2], counters
-    int64_t ws_rows;        // partial rows the workspace holds
-    int64_t n_units;        // arrival counters (batch x KV heads x row blocks)
+    int32_t forced_chunk;
+    float* ws;              // partials: acc [ws_floats], (m, l), then the arrival counters
+    int64_t ws_part_rows;   // partial rows (slot x segment row) the workspace holds
+    int64_t n_units;        // arrival counters (batch x segments per sequence)
     int64_t stride_seq, stride_head, stride_tok;
 };
 
@@ -88,49 +92,24 @@ int row_blocks_of(const kvattn_config& c, int q_len) {
     return (rows + rpb - 1) / rpb;
 }
 
-// Automatic split count for `batch` sequences of up to n_att attended positions,
-// aiming at `target` resident workgroups.
-void auto_plan(const kvattn_config& c, int batch, int q_len, int64_t n_att, int target,
-               int* n_split, int* split_len) {
-    const bool mfma = use_mfma(c, q_len);
-    const int64_t units = (int64_t)(batch > 0 ? batch : 1) * c.num_kv_heads * row_blocks_of(c, q_len);
-    int ns = ceil_div(target, units);
-    const int ns_cap = ceil_div(n_att > 0 ? n_att : 1, mfma ? kMinSplitLenMfma : kMinSplitLen);
-    if (ns > ns_cap) ns = ns_cap;
-    if (ns < 1) ns = 1;
-    if (ns > kMaxSplits) ns = kMaxSplits;
-    int len = ceil_div(n_att > 0 ? n_att : 1, ns);
-    len = ceil_div(len, kSplitQuantum) * kSplitQuantum;
-    *split_len = len;
-    *n_split = ceil_div(n_att > 0 ? n_att : 1, len);
+// Rows of one segment as laid out in the workspace (the kernel instance's row block;
+// the matrix-core kernel pads to whole 16-row tiles).
+int seg_rows_of(const kvattn_config& c, int q_len) {
+    const int rows = rows_of(c, q_len);
+    if (use_mfma(c, q_len)) return (rows + 15) / 16 * 16;
+    return kvattn::valu_rows_per_block(rows);
 }
 
-int64_t workspace_rows(const kvattn_config& c) {
-    // largest batch x splits product the automatic plan can ask for, over every batch
-    // size and q_len the handle accepts; plus room for up to 64 forced splits
-    int64_t best = 0;
-    for (int ql = 1; ql <= c.max_q_len; ++ql) {
-        for (int b = 1; b <= c.max_batch; ++b) {
-            int ns, len;
-            auto_plan(c, b, ql, c.capacity, kMaxResidentWorkgroups, &ns, &len);
-            const int64_t rows = (int64_t)b * ql * c.num_q_heads * ns;
-            if (rows > best) best = rows;
-        }
-    }
-    const int64_t floor_splits = std::min<int64_t>(64, ceil_div(c.capacity, kSplitQuantum));
-    const int64_t fl = (int64_t)c.max_batch * c.max_q_len * c.num_q_heads * floor_splits;
-    return best > fl ? best : fl;
+int64_t segs_per_seq_of(const kvattn_config& c, int q_len) {
+    return (int64_t)c.num_kv_heads * row_blocks_of(c, q_len);
 }
 
-// Arrival counters: one per (sequence, KV head, block of 16 rows).
+// Arrival counters: one per segment.
 int64_t counter_units(const kvattn_config& c) {
-    const int64_t rows = (int64_t)c.max_q_len * (c.num_q_heads / c.num_kv_heads);
-    return (int64_t)c.max_batch * c.num_kv_heads * ((rows + 15) / 16);
-}
-
-size_t workspace_size(const kvattn_config& c, int64_t ws_rows) {
-    return (size_t)ws_rows * (size_t)(c.head_dim + 2) * sizeof(float) +
-           (size_t)counter_units(c) * sizeof(int32_t);
+    int64_t best = 0;
+    for (int ql = 1; ql <= c.max_q_len; ++ql)
+        best = std::max(best, (int64_t)c.max_batch * segs_per_seq_of(c, ql));
+    return best;
 }
 
 int validate_config(const kvattn_config* c) {
@@ -147,6 +126,8 @@ int validate_config(const kvattn_config* c) {
     if (c->capacity < 1) return fail(KVATTN_ERR_INVALID_ARG, "capacity must be >= 1");
     if (c->layout != KVATTN_LAYOUT_TOKEN_MAJOR && c->layout != KVATTN_LAYOUT_HEAD_MAJOR)
         return fail(KVATTN_ERR_INVALID_ARG, "unknown layout");
+    if (c->flags & ~KVATTN_FLAG_DETERMINISTIC)
+        return fail(KVATTN_ERR_INVALID_ARG, "unknown flag bits");
     if (!(c->scale >= 0.0f) || std::isinf(c->scale))
         return fail(KVATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
     switch (c->cache_mode) {
@@ -192,11 +173,8 @@ int validate_decode_args(const kvattn_handle* h, int32_t q_len, int32_t mask_mod
 }
 
 // Workgroups of the kernel instance a decode with q_len would launch that fit on
-// the device at once (occupancy query, cached per q_len).
-int resident_workgroups(kvattn_handle* h, int q_len) {
-    int& r = h->resident[q_len];
-    if (r > 0) return r;
-    const kvattn_config& c = h->cfg;
+// the device at once (occupancy query).
+int resident_for(const kvattn_config& c, int q_len, int num_cus) {
     const int rows = rows_of(c, q_len);
     const bool mfma = use_mfma(c, q_len);
     const void* k = mfma ? kvattn::select_mfma_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
@@ -204,28 +182,61 @@ int resident_workgroups(kvattn_handle* h, int q_len) {
                                                       q_len > 1);
     int per_cu = 0;
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                  &per_cu, k, mfma ? kvattn::kMfmaThreads : kvattn::kValuThreads, 0) != hipSuccess ||
+                  &per_cu, k, mfma ? kvattn::kMfmaThreads : kvattn::valu_threads(rows), 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
-    r = std::min(per_cu * h->num_cus, kMaxResidentWorkgroups);
+    return std::min(per_cu * num_cus, kMaxResidentWorkgroups);
+}
+
+int resident_workgroups(kvattn_handle* h, int q_len) {
+    int& r = h->resident[q_len];
+    if (r <= 0) r = resident_for(h->cfg, q_len, h->num_cus);
     return r;
 }
 
+// Partial rows the workspace needs for decodes with q_len: one slot per workgroup
+// (at most kMaxResidentWorkgroups are launched) plus one per segment (the pieces of
+// a step fill at most that many), each holding a segment's rows.  Host-only: the
+// bound does not depend on the device.
+int64_t part_rows_for(const kvattn_config& c, int q_len) {
+    return ((int64_t)kMaxResidentWorkgroups * kGridFactor +
+            (int64_t)c.max_batch * segs_per_seq_of(c, q_len)) *
+           seg_rows_of(c, q_len);
+}
+
+int64_t workspace_part_rows(const kvattn_config& c) {
+    int64_t best = 0;
+    for (int ql = 1; ql <= c.max_q_len; ++ql) best = std::max(best, part_rows_for(c, ql));
+    return best;
+}
+
+size_t workspace_size(const kvattn_config& c, int64_t part_rows) {
+    return (size_t)part_rows * (size_t)(c.head_dim + 2) * sizeof(float) +
+           (size_t)counter_units(c) * sizeof(int32_t);
+}
+
+// Grid and minimum slice length of a decode with these host arguments.  The work
+// itself is only known on the device (seq_lens); the grid is sized for the most
+// the arguments allow: batch x segments x the longest attended set.
 int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
-             int32_t window, int* n_split, int* split_len) {
+             int32_t window, int* grid, int* min_chunk) {
     const kvattn_config& c = h->cfg;
-    const int64_t n_att = max_attended(c, q_len, mask_mode, n_sink, window);
-    if (h->forced_split_len > 0) {
-        *split_len = h->forced_split_len;
-        *n_split = ceil_div(n_att > 0 ? n_att : 1, h->forced_split_len);
+    const int64_t n_att = std::max<int64_t>(1, max_attended(c, q_len, mask_mode, n_sink, window));
+    const int64_t w_max = std::max<int64_t>(1, (int64_t)h->batch * segs_per_seq_of(c, q_len) * n_att);
+    int64_t g;
+    if (h->forced_chunk > 0) {
+        *min_chunk = h->forced_chunk;
+        g = ceil_div(w_max, h->forced_chunk);
     } else {
-        auto_plan(c, h->batch, q_len, n_att, resident_workgroups(h, q_len), n_split, split_len);
+        *min_chunk = use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk;
+        g = std::min<int64_t>((int64_t)resident_workgroups(h, q_len) * kGridFactor,
+                              ceil_div(w_max, *min_chunk));
     }
-    if (*n_split > 1) {
-        const int64_t need = (int64_t)h->batch * q_len * c.num_q_heads * *n_split;
-        if (need > h->ws_rows)
-            return fail(KVATTN_ERR_CAPACITY, "split count exceeds the handle's workspace");
-    }
+    const int64_t need =
+        (g + (int64_t)h->batch * segs_per_seq_of(c, q_len)) * seg_rows_of(c, q_len);
+    if (need > h->ws_part_rows)
+        return fail(KVATTN_ERR_CAPACITY, "slice count exceeds the handle's workspace");
+    *grid = (int)std::max<int64_t>(1, g);
     return KVATTN_OK;
 }
 
@@ -239,7 +250,7 @@ int kvattn_workspace_bytes(const kvattn_config* cfg, size_t* bytes) {
     int rc = validate_config(cfg);
     if (rc) return rc;
     if (!bytes) return fail(KVATTN_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = workspace_size(*cfg, workspace_rows(*cfg));
+    *bytes = workspace_size(*cfg, workspace_part_rows(*cfg));
     return KVATTN_OK;
 }
 
@@ -253,7 +264,7 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
     h->cfg = *cfg;
     h->stream = nullptr;
     h->batch = cfg->max_batch;
-    h->forced_split_len = 0;
+    h->forced_chunk = 0;
     const int64_t D = cfg->head_dim, H = cfg->num_kv_heads;
     const int64_t unit = cfg->cache_mode == KVATTN_PAGED ? cfg->block_size : cfg->capacity;
     if (cfg->layout == KVATTN_LAYOUT_TOKEN_MAJOR) {
@@ -272,14 +283,14 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
         return fail(KVATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     }
     for (int& r : h->resident) r = 0;
-    h->ws_rows = workspace_rows(*cfg);
+    h->ws_part_rows = workspace_part_rows(*cfg);
     h->n_units = counter_units(*cfg);
     // the merge addresses partials with 32-bit byte offsets
-    if ((double)h->ws_rows * cfg->head_dim * sizeof(float) >= 2147483648.0) {
+    if ((double)h->ws_part_rows * cfg->head_dim * sizeof(float) >= 2147483648.0) {
         delete h;
         return fail(KVATTN_ERR_CAPACITY, "workspace would exceed 2 GiB; lower max_batch or max_q_len");
     }
-    const size_t bytes = workspace_size(*cfg, h->ws_rows);
+    const size_t bytes = workspace_size(*cfg, h->ws_part_rows);
     e = hipMalloc(reinterpret_cast<void**>(&h->ws), bytes);
     if (e != hipSuccess) {
         delete h;
@@ -319,9 +330,9 @@ int kvattn_set_batch(kvattn_handle* h, int32_t batch) {
 
 int kvattn_set_split_len(kvattn_handle* h, int32_t split_len) {
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
-    if (split_len < 0 || split_len % kSplitQuantum)
+    if (split_len < 0 || split_len % kChunkQuantum)
         return fail(KVATTN_ERR_INVALID_ARG, "split_len must be 0 or a positive multiple of 64");
-    h->forced_split_len = split_len;
+    h->forced_chunk = split_len;
     return KVATTN_OK;
 }
 
@@ -330,11 +341,11 @@ int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_si
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
     int rc = validate_decode_args(h, q_len, mask_mode, n_sink, window);
     if (rc) return rc;
-    int ns, len;
-    rc = plan_for(h, q_len, mask_mode, n_sink, window, &ns, &len);
+    int grid, chunk;
+    rc = plan_for(h, q_len, mask_mode, n_sink, window, &grid, &chunk);
     if (rc) return rc;
-    if (n_split) *n_split = ns;
-    if (split_len) *split_len = len;
+    if (n_split) *n_split = grid;
+    if (split_len) *split_len = chunk;
     if (kernel) *kernel = use_mfma(h->cfg, q_len) ? 1 : 0;
     return KVATTN_OK;
 }
@@ -342,7 +353,7 @@ int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_si
 static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const void* q,
                         const void* k, const void* v, const int32_t* bt, const int32_t* sl,
                         int32_t q_len, int32_t mask_mode, int32_t n_sink, int32_t window,
-                        void* out, int n_split, int split_len) {
+                        void* out, int min_chunk) {
     const kvattn_config& c = h->cfg;
     p.q = q;
     p.k = k;
@@ -351,8 +362,8 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.seq_lens = sl;
     p.out = out;
     p.ws_acc = h->ws;
-    p.ws_ml = h->ws + h->ws_rows * c.head_dim;
-    p.counters = reinterpret_cast<int32_t*>(h->ws + h->ws_rows * (c.head_dim + 2));
+    p.ws_ml = h->ws + h->ws_part_rows * c.head_dim;
+    p.counters = reinterpret_cast<int32_t*>(h->ws + h->ws_part_rows * (c.head_dim + 2));
     p.stride_seq = h->stride_seq;
     p.stride_head = h->stride_head;
     p.stride_tok = h->stride_tok;
@@ -370,8 +381,11 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.log2_block = c.cache_mode == KVATTN_PAGED ? ilog2(c.block_size) : 0;
     p.num_blocks = c.cache_mode == KVATTN_PAGED ? c.num_blocks : 0;
     p.blocks_per_seq = c.cache_mode == KVATTN_PAGED ? c.capacity / c.block_size : 0;
-    p.n_split = n_split;
-    p.split_len = split_len;
+    p.row_blocks = row_blocks_of(c, q_len);
+    p.segs_per_seq = (int32_t)segs_per_seq_of(c, q_len);
+    p.seg_rows = seg_rows_of(c, q_len);
+    p.min_chunk = min_chunk;
+    p.deterministic = (c.flags & KVATTN_FLAG_DETERMINISTIC) ? 1 : 0;
     const float scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
 }
@@ -389,15 +403,16 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
         return fail(KVATTN_ERR_INVALID_ARG, "block_table must be given exactly for a paged cache");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return fail(KVATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
-    int ns, len;
-    rc = plan_for(h, q_len, mask_mode, n_sink, window, &ns, &len);
+    int grid, chunk;
+    rc = plan_for(h, q_len, mask_mode, n_sink, window, &grid, &chunk);
     if (rc) return rc;
     kvattn::DecodeParams p;
     fill_params(h, p, q, k_cache, v_cache, block_table, seq_lens, q_len, mask_mode, n_sink,
-                window, out, ns, len);
-    hipError_t e = use_mfma(h->cfg, q_len)
-                       ? kvattn::launch_decode_mfma(p, h->cfg.dtype, h->cfg.head_dim, h->stream)
-                       : kvattn::launch_decode_valu(p, h->cfg.dtype, h->cfg.head_dim, h->stream);
+                window, out, chunk);
+    hipError_t e =
+        use_mfma(h->cfg, q_len)
+            ? kvattn::launch_decode_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
+            : kvattn::launch_decode_valu(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream);
     if (e != hipSuccess)
         return fail(KVATTN_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return KVATTN_OK;
@@ -416,7 +431,7 @@ int kvattn_debug_gather(kvattn_handle* h, const int32_t* block_table, const int3
         return fail(KVATTN_ERR_INVALID_ARG, "block_table must be given exactly for a paged cache");
     kvattn::DecodeParams p;
     fill_params(h, p, nullptr, nullptr, nullptr, block_table, seq_lens, q_len, mask_mode, n_sink,
-                window, nullptr, 1, 1 << 30);
+                window, nullptr, 1 << 30);
     hipError_t e = kvattn::launch_debug_gather(p, max_slots, slots_out, counts_out, h->stream);
     if (e != hipSuccess)
         return fail(KVATTN_ERR_HIP, std::string("gather launch: ") + hipGetErrorString(e));

@@ -8,13 +8,16 @@
 namespace kvattn {
 
 // Vector-ALU split-KV kernel (any row count; rows above 16 run in blocks of 16).
-hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
+// `grid` workgroups share the step's work in equal slices.
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, int grid,
+                              hipStream_t st);
 int valu_rows_per_block(int rows);
+int valu_threads(int rows);  // workgroup size of the instance serving `rows`
 const void* select_valu_kernel(int dtype, int head_dim, int rows, int cache_mode, bool masked);
-constexpr int kValuThreads = 256;
 
 // Matrix-core split-KV kernel for 16 to 64 rows per KV head (f16 / bf16).
-hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,
+                              hipStream_t st);
 bool mfma_supported(int dtype, int head_dim, int rows);
 const void* select_mfma_kernel(int dtype, int head_dim, int rows, int cache_mode);
 constexpr int kMfmaThreads = 256;

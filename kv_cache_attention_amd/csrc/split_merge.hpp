@@ -1,21 +1,22 @@
 // Log-sum-exp merge of split-KV partials, run by the last workgroup of a
-// (sequence, KV head, row block) to finish.
+// segment (sequence, KV head, row block) to finish its piece.
 //
-// Each split s leaves, per row, its unnormalised accumulator acc_s[d] and its
-// running max m_s and sum l_s (exp2 domain).  The row's result is
-//     M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  out = sum_s acc_s 2^(m_s - M) / L
+// Each piece k of a segment leaves, per row r, its unnormalised accumulator
+// acc_k[d] and its running max m_k and sum l_k (exp2 domain) in workspace slot
+// slot0 + k, row r (slot-major: index (slot * seg_rows + r)).  The row's result is
+//     M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k acc_k 2^(m_k - M) / L
 // - the same rescaling identity the online softmax applies across tiles (Flash
 // Attention section of the nextadmin.net lesson "KV cache and Flash Attention"),
-// applied once more across splits.  Empty splits (m = -inf, l = 0) weigh 0.
+// applied once more across pieces.  Empty pieces (m = -inf, l = 0) weigh 0.
 //
-// Arrival protocol: every workgroup of a unit writes its partial with
+// Arrival protocol: every workgroup of a segment writes its partial with
 // device-scope stores (they write through the per-XCD L2 to the device-coherent
-// level), waits until they are acknowledged, and takes a ticket from the unit's
-// counter with a device-scope atomic.  The workgroup that draws the last ticket
-// reads the partials with device-scope loads (which do not hit a possibly stale
-// L2 line), merges, and puts the counter back to zero for the next call.  No
-// L2-wide write-back or invalidate is needed - a per-workgroup full-L2 fence
-// would cost more than the whole split - and nothing waits on another
+// level), waits until they are acknowledged, and takes a ticket from the
+// segment's counter with a device-scope atomic.  The workgroup that draws the
+// last ticket reads the partials with device-scope loads (which do not hit a
+// possibly stale L2 line), merges, and puts the counter back to zero for the next
+// call.  No L2-wide write-back or invalidate is needed - a per-workgroup full-L2
+// fence would cost more than the whole piece - and nothing waits on another
 // workgroup, so no schedule can hang.
 #pragma once
 
@@ -98,11 +99,12 @@ struct MergeSmem {
     float4 red[THREADS];
 };
 
-// Called by every thread of the workgroup after it wrote its partial.  Returns
-// after the merge (last workgroup) or right away (the others).
+// Called by every thread of the workgroup after it wrote its partial of rows
+// row0 .. row0 + NROWS - 1 of KV head kvh into slot slot0 + (its piece).  Returns
+// after the merge (last workgroup of the segment) or right away (the others).
 template <int DT, int D, int NROWS, int THREADS>
-__device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0, int unit,
-                                 int nvalid, MergeSmem<NROWS, THREADS>& sm) {
+__device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0, int64_t unit,
+                                 int64_t slot0, int nvalid, MergeSmem<NROWS, THREADS>& sm) {
     static_assert(THREADS % 64 == 0, "whole waves");
     __shared__ int s_last;
     const int tid = threadIdx.x;
@@ -113,7 +115,7 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
     if (!s_last) return;
 
     constexpr float NEG_INF = -__builtin_inff();
-    const int n_split = p.n_split;
+    const int NR = p.seg_rows;  // partial k of row r: index (slot0 + k) * NR + r
     const PartialReader rd(p);
 
     // per row: M and L over the splits.  G lanes per row (aligned groups within a
@@ -125,14 +127,14 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
     {
         const int r = tid / G, g = tid % G;
         const bool act = r < NROWS && row0 + r < p.rows;
-        const int64_t part0 = act ? row_id_of(p, b, kvh, row0 + r) * n_split : 0;
+        const int64_t part0 = act ? slot0 * NR + r : 0;
         float mx = NEG_INF, ls = 0.0f;
         for (int sp0 = g; sp0 < nvalid; sp0 += 8 * G) {
             float2 v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int sp = sp0 + u * G;
-                v[u] = rd.ml2(part0 + (sp < nvalid ? sp : g));
+                v[u] = rd.ml2(part0 + (int64_t)(sp < nvalid ? sp : g) * NR);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -180,7 +182,7 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
         e4[k] = in ? e : 0;
         r[k] = e4[k] / (D / 4);
         live[k] = in && row0 + r[k] < p.rows;
-        part0[k] = live[k] ? row_id_of(p, b, kvh, row0 + r[k]) * n_split : 0;
+        part0[k] = live[k] ? slot0 * NR + r[k] : 0;
         mu[k] = live[k] ? sm.M[r[k]] : 0.0f;
         a[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -193,7 +195,7 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
             const int spc = sp < nvalid ? sp : sg;  // clamped: a valid partial, weight 0
 #pragma unroll
             for (int k = 0; k < EPT; ++k) {
-                const int64_t part = part0[k] + spc;
+                const int64_t part = part0[k] + (int64_t)spc * NR;
                 v[u][k] = rd.acc4(part * D + (e4[k] % (D / 4)) * 4);
                 w[u][k] = rd.ml2(part).x;
             }
@@ -229,7 +231,7 @@ __device__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0
         if (sg == 0 && live[k]) {
             const float L = sm.L[r[k]];
             const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-            const int64_t o = (part0[k] / n_split) * D + (e4[k] % (D / 4)) * 4;
+            const int64_t o = row_id_of(p, b, kvh, row0 + r[k]) * D + (e4[k] % (D / 4)) * 4;
             store_elem<DT>(p.out, o, a[k].x * inv);
             store_elem<DT>(p.out, o + 1, a[k].y * inv);
             store_elem<DT>(p.out, o + 2, a[k].z * inv);

@@ -95,9 +95,26 @@ def test_page_permutation_is_bit_identical():
     v2[perm] = inp["v_cache"]
     d1 = gh.to_device(inp)
     d2 = dict(d1, block_table=bt2.cuda(), k_cache=k2.cuda(), v_cache=v2.cuda())
-    o1 = gh.run(case, d1)
-    o2 = gh.run(case, d2)
+    o1 = gh.run(case, d1, handle=kb.KVAttn.for_case(case, deterministic=True))
+    o2 = gh.run(case, d2, handle=kb.KVAttn.for_case(case, deterministic=True))
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    # the default (shared tile queue) mode agrees to rounding
+    o3 = gh.run(case, d2)
+    gh.check(o3, o1.double().cpu().numpy(), case.dtype, "paged_small/queue-vs-fixed")
+
+
+@pytest.mark.parametrize("name", ["decode_7b_small", "sink_window_small", "paged_small"])
+def test_deterministic_mode_repeats_bit_for_bit(name):
+    """With KVATTN_FLAG_DETERMINISTIC, repeated decodes of the same inputs (several tiles
+    per wave, several pieces per sequence) give identical bits."""
+    case = SMALL[name]
+    print(f"case={name} deterministic", flush=True)
+    d = gh.to_device(workloads.make_inputs(case))
+    h = kb.KVAttn.for_case(case, deterministic=True)
+    h.set_split_len(64)
+    outs = [gh.run(case, d, handle=h) for _ in range(4)]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
 @pytest.mark.parametrize("name", ["sink_window_small", "paged_small", "decode_7b_small",
