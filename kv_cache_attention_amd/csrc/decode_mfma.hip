@@ -125,7 +125,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
 
     const int wg = blockIdx.x;
     const int n_wg = gridDim.x;
-    const WgRange range = plan_range<MFMA_THREADS>(p, wg, n_wg);
+    const FlatPlan fp = plan_flat<MFMA_THREADS>(p, n_wg);
 
     const int tid = threadIdx.x;
     const int wave = tid / 64;
@@ -133,7 +133,8 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     const int lr = l % 16;  // operand row / output column
     const int lq = l / 16;  // operand k-group / output row group
 
-    for_each_piece(p, range, wg, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
+    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
     const int b = pc.b;
     const int kvh = pc.seg;
     const int32_t j0 = pc.ja;
@@ -444,6 +445,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         arrive_and_merge<DT, D, NQ, MFMA_THREADS>(p, b, kvh, 0, pc.unit, pc.slot0, pc.nparts, msm);
         __syncthreads();  // LDS is reused by the next piece
     }
+    });
     });
     zero_empty_sequences<DT, MFMA_THREADS, D>(p, wg, n_wg);
 }

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
 
     const int wg = blockIdx.x;
     const int n_wg = gridDim.x;
-    const WgRange range = plan_range<THREADS>(p, wg, n_wg);
+    const FlatPlan fp = plan_flat<THREADS>(p, n_wg);
 
     const int tid = threadIdx.x;
     const int wave = tid / 64;
@@ -129,7 +129,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
     const int64_t dv = reinterpret_cast<const char*>(p.v) - reinterpret_cast<const char*>(p.k);
     const float c = p.scale_log2;
 
-    for_each_piece(p, range, wg, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
+    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
         const int b = pc.b;
         const int kvh = pc.seg / p.row_blocks;
         const int rb = pc.seg - kvh * p.row_blocks;
@@ -367,6 +368,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             arrive_and_merge<DT, D, ROWS, THREADS>(p, b, kvh, rb * ROWS, pc.unit, pc.slot0,
                                                    pc.nparts, msm);
         __syncthreads();  // LDS is reused by the next piece
+    });
     });
     zero_empty_sequences<DT, THREADS, D>(p, wg, n_wg);
 }

@@ -24,6 +24,7 @@ struct DecodeParams {
     float* ws_acc;        // [slots, seg_rows, D]  partials of split segments (unnormalised)
     float* ws_ml;         // [slots, seg_rows, 2]  (running max m, sum l), log2 domain
     int32_t* counters;    // [batch, Hkv, row blocks] arrivals per segment, 0 between calls
+    int32_t* queue;       // [2]: units taken beyond the first per workgroup, workgroups done
     int64_t stride_seq;   // elements: sequence (contiguous/ring) or block (paged)
     int64_t stride_head;  // elements: KV head
     int64_t stride_tok;   // elements: slot within a sequence / block
@@ -33,7 +34,8 @@ struct DecodeParams {
     int32_t row_blocks;   // segments per (sequence, KV head): blocks of query rows
     int32_t segs_per_seq; // num_kv_heads * row_blocks
     int32_t seg_rows;     // rows per segment as laid out in the workspace
-    int32_t min_chunk;    // smallest share of work per workgroup (positions)
+    int32_t min_chunk;    // smallest unit (positions)
+    int32_t units_per_wg; // units per workgroup the flat range is cut into
     int32_t deterministic;  // waves take fixed tiles instead of a shared queue
     float scale_log2;     // softmax scale * log2(e): scores are kept in the exp2 domain
 };

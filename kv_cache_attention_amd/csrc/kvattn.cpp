@@ -24,16 +24,17 @@ int fail(int code, const std::string& msg) {
 }
 
 // Work decomposition: the flat list of (sequence, KV head, row block) segments is
-// cut into equal slices, one per workgroup, with as many workgroups as the GPU
-// holds resident at once for the kernel instance (occupancy x compute units), so
-// the step runs in one round with no tail.  A slice is at least kMinChunk
-// positions (kMinChunkMfma for the matrix-core kernel, whose per-piece epilogue
-// is heavier).  The split points are placed on the device from seq_lens.
-#ifndef KVATTN_GRID_FACTOR
-#define KVATTN_GRID_FACTOR 1
+// cut into equal units, about kUnitsPerWg per workgroup, with as many workgroups
+// as the GPU holds resident at once for the kernel instance (occupancy x compute
+// units); workgroups take units from a device-wide queue.  A unit is at least
+// kMinChunk positions (kMinChunkMfma for the matrix-core kernel, whose per-piece
+// epilogue is heavier).  The split points are placed on the device from seq_lens.
+#ifndef KVATTN_UNITS_PER_WG
+#define KVATTN_UNITS_PER_WG 1
 #endif
-constexpr int kMaxResidentWorkgroups = 2048;
-constexpr int kGridFactor = KVATTN_GRID_FACTOR;  // workgroups launched per resident slot
+constexpr int kMaxResidentWorkgroups = 1024;
+constexpr int kMinForcedUnits = 512;
+constexpr int kUnitsPerWg = KVATTN_UNITS_PER_WG;  // units of the flat range per workgroup
 constexpr int kMinChunk = 256;
 constexpr int kMinChunkMfma = 512;
 constexpr int kChunkQuantum = 64;
@@ -194,14 +195,19 @@ int resident_workgroups(kvattn_handle* h, int q_len) {
     return r;
 }
 
-// Partial rows the workspace needs for decodes with q_len: one slot per workgroup
-// (at most kMaxResidentWorkgroups are launched) plus one per segment (the pieces of
-// a step fill at most that many), each holding a segment's rows.  Host-only: the
-// bound does not depend on the device.
+// Partial rows the workspace needs for decodes with q_len: one slot per unit plus
+// one per segment (the pieces of a step fill at most that many), each holding a
+// segment's rows.  Units: at most kUnitsPerWg per launched workgroup (at most
+// kMaxResidentWorkgroups), and no more than the longest possible flat range holds
+// at the default minimum unit; forced unit lengths (tests) may use up to
+// kMinForcedUnits.  Host-only: the bound does not depend on the device.
 int64_t part_rows_for(const kvattn_config& c, int q_len) {
-    return ((int64_t)kMaxResidentWorkgroups * kGridFactor +
-            (int64_t)c.max_batch * segs_per_seq_of(c, q_len)) *
-           seg_rows_of(c, q_len);
+    const int64_t segs = (int64_t)c.max_batch * segs_per_seq_of(c, q_len);
+    const int64_t w_max = segs * max_attended(c, q_len, KVATTN_MASK_CAUSAL, 0, 0);
+    const int64_t by_len = ceil_div(w_max, use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk);
+    const int64_t units = std::min<int64_t>((int64_t)kMaxResidentWorkgroups * kUnitsPerWg,
+                                            std::max<int64_t>(by_len, kMinForcedUnits));
+    return (units + segs) * seg_rows_of(c, q_len);
 }
 
 int64_t workspace_part_rows(const kvattn_config& c) {
@@ -210,12 +216,13 @@ int64_t workspace_part_rows(const kvattn_config& c) {
     return best;
 }
 
+// acc and (m, l) of the partials, one arrival counter per segment, the unit queue.
 size_t workspace_size(const kvattn_config& c, int64_t part_rows) {
     return (size_t)part_rows * (size_t)(c.head_dim + 2) * sizeof(float) +
-           (size_t)counter_units(c) * sizeof(int32_t);
+           (size_t)(counter_units(c) + 2) * sizeof(int32_t);
 }
 
-// Grid and minimum slice length of a decode with these host arguments.  The work
+// Grid and minimum unit length of a decode with these host arguments.  The work
 // itself is only known on the device (seq_lens); the grid is sized for the most
 // the arguments allow: batch x segments x the longest attended set.
 int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
@@ -223,19 +230,15 @@ int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
     const kvattn_config& c = h->cfg;
     const int64_t n_att = std::max<int64_t>(1, max_attended(c, q_len, mask_mode, n_sink, window));
     const int64_t w_max = std::max<int64_t>(1, (int64_t)h->batch * segs_per_seq_of(c, q_len) * n_att);
-    int64_t g;
-    if (h->forced_chunk > 0) {
-        *min_chunk = h->forced_chunk;
-        g = ceil_div(w_max, h->forced_chunk);
-    } else {
-        *min_chunk = use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk;
-        g = std::min<int64_t>((int64_t)resident_workgroups(h, q_len) * kGridFactor,
-                              ceil_div(w_max, *min_chunk));
-    }
+    *min_chunk = h->forced_chunk > 0 ? h->forced_chunk
+                                     : (use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk);
+    const int64_t units_max = ceil_div(w_max, *min_chunk);  // units are >= min_chunk
+    const int64_t g = std::min<int64_t>(resident_workgroups(h, q_len), units_max);
+    const int64_t units = h->forced_chunk > 0 ? units_max : std::min<int64_t>(units_max, g * kUnitsPerWg);
     const int64_t need =
-        (g + (int64_t)h->batch * segs_per_seq_of(c, q_len)) * seg_rows_of(c, q_len);
+        (units + (int64_t)h->batch * segs_per_seq_of(c, q_len)) * seg_rows_of(c, q_len);
     if (need > h->ws_part_rows)
-        return fail(KVATTN_ERR_CAPACITY, "slice count exceeds the handle's workspace");
+        return fail(KVATTN_ERR_CAPACITY, "unit count exceeds the handle's workspace");
     *grid = (int)std::max<int64_t>(1, g);
     return KVATTN_OK;
 }
@@ -364,6 +367,7 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.ws_acc = h->ws;
     p.ws_ml = h->ws + h->ws_part_rows * c.head_dim;
     p.counters = reinterpret_cast<int32_t*>(h->ws + h->ws_part_rows * (c.head_dim + 2));
+    p.queue = p.counters + h->n_units;
     p.stride_seq = h->stride_seq;
     p.stride_head = h->stride_head;
     p.stride_tok = h->stride_tok;
@@ -385,6 +389,7 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.segs_per_seq = (int32_t)segs_per_seq_of(c, q_len);
     p.seg_rows = seg_rows_of(c, q_len);
     p.min_chunk = min_chunk;
+    p.units_per_wg = h->forced_chunk > 0 ? 1 << 30 : kUnitsPerWg;  // forced: units of exactly min_chunk
     p.deterministic = (c.flags & KVATTN_FLAG_DETERMINISTIC) ? 1 : 0;
     const float scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;

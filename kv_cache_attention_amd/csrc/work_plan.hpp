@@ -4,35 +4,37 @@
 // block of query rows), each holding the count_b positions sequence b attends
 // (all KV heads and row blocks of a sequence have the same count).  Laid end to
 // end in (b, KV head, row block) order they form one flat range of
-// W = sum_b count_b * segs_per_seq position-units.  Workgroup w of the grid takes
-// the slice [w * chunk, (w + 1) * chunk), chunk = max(ceil(W / grid), min_chunk):
-// every workgroup streams the same number of K/V rows whatever the spread of
-// sequence lengths, and the grid is sized by the host to what the GPU holds at
-// once, so the whole step runs in a single resident round.
+// W = sum_b count_b * segs_per_seq position-units, cut into n_units equal units
+// of usz positions, about units_per_wg per workgroup of a grid sized by the host
+// to what the GPU holds at once.  Workgroups take units from a device-wide queue,
+// so the step ends when the memory system has streamed everything, not when the
+// most poorly served compute unit has finished a fixed share.
 //
-// A slice crosses segment boundaries: its pieces are processed one after the
+// A unit crosses segment boundaries: its pieces are processed one after the
 // other.  A piece that is a whole segment writes the final rows; otherwise it
 // writes a partial (unnormalised accumulator, running max and sum) and the last
 // piece of the segment to finish merges them (split_merge.hpp).  Walking the
-// pieces in flat order, both the workgroup index and the segment index never
-// decrease and at least one grows at each step, so slot = workgroup + segment is
-// a distinct workspace slot per piece; the pieces of one segment occupy
-// consecutive slots.  The slot count is bounded by grid + segments.
+// pieces in flat order, both the unit index and the segment index never decrease
+// and at least one grows at each step, so slot = unit + segment is a distinct
+// workspace slot per piece; the pieces of one segment occupy consecutive slots.
+// The slot count is bounded by units + segments.
 //
 // Nothing here needs the host to know the lengths: each workgroup reads seq_lens
-// (a scan over the batch in LDS) before its first K/V load.
+// (a scan over the batch) before its first K/V load.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace kvattn {
 
-struct WgRange {
-    int64_t total;  // W
-    int64_t chunk;
-    int64_t x0, x1;  // this workgroup's flat slice (empty when x0 >= x1)
-    int32_t b;       // sequence holding x0
-    int64_t off_b;   // flat offset of sequence b
+// Per-thread view of the flat range after the scan over the batch: thread t owns
+// sequences [b0, b0 + per) and their flat offsets [excl, excl + mine).
+struct FlatPlan {
+    int64_t total;   // W
+    int64_t usz;     // positions per unit (the slices workgroups take)
+    int64_t n_units;
+    int b0, per;
+    int64_t excl, mine;
 };
 
 // Flat work of sequence b: attended positions x segments per sequence.
@@ -41,18 +43,17 @@ __device__ __forceinline__ int64_t seq_work(const DecodeParams& p, int b) {
 }
 
 template <int THREADS>
-__device__ __forceinline__ WgRange plan_range(const DecodeParams& p, int wg, int n_wg) {
+__device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     static_assert(THREADS % 64 == 0 && THREADS <= 1024, "whole waves");
     constexpr int NW = THREADS / 64;
     __shared__ int64_t s_part[NW];
-    __shared__ int32_t s_b;
-    __shared__ int64_t s_off;
     const int tid = threadIdx.x;
-    const int per = (p.batch + THREADS - 1) / THREADS;  // sequences per thread
-    const int b0 = tid * per;
+    FlatPlan f;
+    f.per = (p.batch + THREADS - 1) / THREADS;  // sequences per thread
+    f.b0 = tid * f.per;
     int64_t mine = 0;
-    for (int k = 0; k < per; ++k)
-        if (b0 + k < p.batch) mine += seq_work(p, b0 + k);
+    for (int k = 0; k < f.per; ++k)
+        if (f.b0 + k < p.batch) mine += seq_work(p, f.b0 + k);
     // inclusive scan over the wave, then across waves
     const int lane = tid & 63;
     int64_t inc = mine;
@@ -70,23 +71,34 @@ __device__ __forceinline__ WgRange plan_range(const DecodeParams& p, int wg, int
         before += w < (tid >> 6) ? v : 0;
         total += v;
     }
-    const int64_t excl = before + inc - mine;  // flat offset of sequence b0
+    f.excl = before + inc - mine;
+    f.mine = mine;
+    f.total = total;
+    const int64_t units = (int64_t)n_wg * p.units_per_wg;
+    int64_t usz = (total + units - 1) / units;
+    if (usz < p.min_chunk) usz = p.min_chunk;
+    f.usz = (usz + 15) & ~(int64_t)15;
+    f.n_units = (total + f.usz - 1) / f.usz;
+    return f;
+}
 
-    WgRange r;
-    r.total = total;
-    int64_t chunk = (total + n_wg - 1) / n_wg;
-    if (chunk < p.min_chunk) chunk = p.min_chunk;
-    r.chunk = (chunk + 15) & ~(int64_t)15;
-    r.x0 = (int64_t)wg * r.chunk;
-    r.x1 = min(r.x0 + r.chunk, total);
-    // the thread whose sequences hold x0 names the exact one (sequences with no
-    // work hold no flat offset, so exactly one thread matches)
-    if (r.x0 < total && excl <= r.x0 && r.x0 < excl + mine) {
-        int64_t off = excl;
-        for (int k = 0; k < per; ++k) {
-            const int64_t w = seq_work(p, b0 + k);
-            if (r.x0 < off + w) {
-                s_b = b0 + k;
+// The sequence holding flat index x (< total) and its flat offset, found by the
+// thread whose sequences hold x (sequences with no work hold no flat offset, so
+// exactly one thread matches).  Every thread of the workgroup must call it.
+struct SeqAt {
+    int b;
+    int64_t off;
+};
+__device__ __forceinline__ SeqAt seq_at(const DecodeParams& p, const FlatPlan& f, int64_t x) {
+    __shared__ int32_t s_b;
+    __shared__ int64_t s_off;
+    __syncthreads();  // earlier readers of s_b / s_off are done
+    if (f.excl <= x && x < f.excl + f.mine) {
+        int64_t off = f.excl;
+        for (int k = 0; k < f.per; ++k) {
+            const int64_t w = seq_work(p, f.b0 + k);
+            if (x < off + w) {
+                s_b = f.b0 + k;
                 s_off = off;
                 break;
             }
@@ -94,12 +106,10 @@ __device__ __forceinline__ WgRange plan_range(const DecodeParams& p, int wg, int
         }
     }
     __syncthreads();
-    r.b = r.x0 < total ? s_b : 0;
-    r.off_b = r.x0 < total ? s_off : 0;
-    return r;
+    return SeqAt{s_b, s_off};
 }
 
-// One piece of a slice: positions [ja, jb) of the attended list of segment
+// One piece of a unit: positions [ja, jb) of the attended list of segment
 // `seg` (= kvh * row_blocks + row block) of sequence b.
 struct Piece {
     int b;
@@ -111,16 +121,18 @@ struct Piece {
     int part;       // this piece's index among them
 };
 
-// Calls f(piece, span) for each piece of the slice, in flat order.
+// Calls f(piece, span) for each piece of unit u, in flat order.
 template <typename F>
-__device__ __forceinline__ void for_each_piece(const DecodeParams& p, const WgRange& r, int wg,
-                                               F&& f) {
-    if (r.x0 >= r.x1) return;
-    int b = r.b;
-    int64_t off_b = r.off_b;
+__device__ __forceinline__ void for_each_piece(const DecodeParams& p, const FlatPlan& fp,
+                                               int64_t u, F&& f) {
+    const int64_t x0 = u * fp.usz;
+    const int64_t x1 = min(x0 + fp.usz, fp.total);
+    const SeqAt at = seq_at(p, fp, x0);
+    int b = at.b;
+    int64_t off_b = at.off;
     SeqSpan s = seq_span(p, b);
-    int64_t x = r.x0;
-    while (x < r.x1) {
+    int64_t x = x0;
+    while (x < x1) {
         const int64_t wb = (int64_t)s.count * p.segs_per_seq;
         if (x >= off_b + wb) {  // past sequence b (or b holds nothing): next sequence
             off_b += wb;
@@ -133,15 +145,47 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const WgRa
         pc.seg = (int)((x - off_b) / s.count);
         const int64_t seg0 = off_b + (int64_t)pc.seg * s.count;
         pc.ja = (int32_t)(x - seg0);
-        pc.jb = (int32_t)min<int64_t>(s.count, r.x1 - seg0);
-        const int64_t first = seg0 / r.chunk;
-        const int64_t last = (seg0 + s.count - 1) / r.chunk;
+        pc.jb = (int32_t)min<int64_t>(s.count, x1 - seg0);
+        const int64_t first = seg0 / fp.usz;
+        const int64_t last = (seg0 + s.count - 1) / fp.usz;
         pc.unit = (int64_t)b * p.segs_per_seq + pc.seg;
         pc.slot0 = first + pc.unit;
         pc.nparts = (int)(last - first + 1);
-        pc.part = (int)(wg - first);
+        pc.part = (int)(u - first);
         f(pc, s);
         x = seg0 + pc.jb;
+    }
+}
+
+// Runs body(u) for every unit this workgroup takes.  Workgroup w starts with unit
+// w; further units come from a device-wide counter (one atomic per unit, issued a
+// unit ahead), so workgroups that the memory system serves faster take more.  In
+// deterministic mode workgroup w takes units w, w + grid, ...  The last workgroup
+// to leave puts the counter back to zero for the next call: every workgroup
+// counts itself out only after its final take, so no take can follow the reset.
+template <typename F>
+__device__ __forceinline__ void for_each_unit(const DecodeParams& p, const FlatPlan& fp, int wg,
+                                              int n_wg, F&& body) {
+    __shared__ int64_t s_next_unit[2];  // by iteration parity: a slot is rewritten only
+                                        // after a barrier that follows every read of it
+    int64_t u = wg;
+    for (int it = 0; u < fp.n_units; ++it) {
+        int64_t next = 0;
+        if (threadIdx.x == 0)  // issued now, its result is waited for only after the unit
+            next = p.deterministic ? u + n_wg
+                                   : (int64_t)n_wg + __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED,
+                                                                            __HIP_MEMORY_SCOPE_AGENT);
+        body(u);
+        if (threadIdx.x == 0) s_next_unit[it & 1] = next;
+        __syncthreads();
+        u = s_next_unit[it & 1];
+    }
+    if (threadIdx.x == 0 && !p.deterministic) {
+        if (__hip_atomic_fetch_add(p.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            n_wg - 1) {
+            __hip_atomic_store(p.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
