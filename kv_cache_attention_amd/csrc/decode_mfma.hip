@@ -114,14 +114,17 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     // V staging (per wave) during the loop, reused for the cross-wave merge after it;
     // the Q^T operand fragments, shared by the four waves.
     constexpr int SMEM_V = MFMA_WAVES * G::VBUF;
-    static_assert(NQ * D * 4 <= SMEM_V, "merge buffer must fit in the staging area");
-    __shared__ __attribute__((aligned(16))) char smem[SMEM_V];
+    // O merge buffer [waves][NQ][OROW] floats: rows padded by 4 floats so the 16 rows a
+    // wave's lanes write at once start on 16 different 4-bank groups
+    constexpr int OROW = D + 4;
+    constexpr int SMEM_O = MFMA_WAVES * NQ * OROW * 4;
+    constexpr int SMEM = SMEM_V > SMEM_O ? SMEM_V : SMEM_O;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
     __shared__ u32x4 qsm[G::QFRAGS * 64];
     __shared__ float sm_m[MFMA_WAVES][NQ];
     __shared__ float sm_l[MFMA_WAVES][NQ];
 
-    __shared__ float sm_f[MFMA_WAVES][NQ];
-    __shared__ float sm_M[NQ], sm_L[NQ];
+    __shared__ int s_next_tile;
 
     const int wg = blockIdx.x;
     const int n_wg = gridDim.x;
@@ -193,10 +196,6 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         }
     };
 
-    const int32_t step = MFMA_WAVES * TILE;
-    int32_t tb = j0 + wave * TILE;
-    // One register buffer each for K and V: the next tile's V is loaded as soon as
-    // this tile's V sits in LDS, the next K as soon as S^T has consumed this K.
     // Q^T operand fragments (LDS): fragment f = qt*KS + ks; lane l holds row
     // qt*16 + l%16, d chunk (ks*4 + l/16)*8.  Loaded first, stored after the first
     // tile's loads are in flight.
@@ -218,10 +217,28 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         }
     }
 
+    // Waves take tiles of TILE positions from a counter in LDS (wave w starts with
+    // tile w), so a wave the memory system serves faster takes more tiles; in
+    // deterministic mode wave w takes tiles w, w + waves, ...  The next tile is
+    // known one tile ahead, and the one after is requested at the top of each
+    // iteration, so the LDS atomic's latency is not waited for.
+    const int32_t n_tiles = (j1 - j0 + TILE - 1) / TILE;
+    if (tid == 0) s_next_tile = MFMA_WAVES;
+    auto grab = [&](int32_t after) __attribute__((always_inline)) -> int32_t {
+        if (p.deterministic) return after + MFMA_WAVES;
+        int32_t t = 0;
+        if (l == 0)
+            t = __hip_atomic_fetch_add(&s_next_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return __builtin_amdgcn_readfirstlane(t);
+    };
+
+    // One register buffer each for K and V: the next tile's V is loaded as soon as
+    // this tile's V sits in LDS, the next K as soon as S^T has consumed this K.
     u32x4 kc[2][KS], vr[NV];
-    if (tb < j1) {
-        load_k(tb, kc);
-        load_v(tb, vr);
+    int32_t cur = wave;
+    if (cur < n_tiles) {
+        load_k(j0 + cur * TILE, kc);
+        load_v(j0 + cur * TILE, vr);
     }
 
     // Q staged from registers once the loads above are issued (the Q loads were
@@ -229,7 +246,8 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
 #pragma unroll
     for (int k = 0; k < QPT; ++k)
         if (tid + k * MFMA_THREADS < G::QFRAGS * 64) qsm[tid + k * MFMA_THREADS] = qreg[k];
-    __syncthreads();
+    __syncthreads();  // Q^T and the tile counter are ready
+    int32_t nxt = cur < n_tiles ? grab(cur) : n_tiles;
 
     // new row i sits at T - q_len + i; rows see positions <= their own
     const int32_t P0 = s.T - p.q_len;
@@ -242,18 +260,23 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     }
     const float c = p.scale_log2;
 
-    for (; tb < j1; tb += step) {
-        // stage this tile's V rows in LDS: [position][d], padded rows, 16-byte writes
+    while (cur < n_tiles) {
+        const int32_t tb = j0 + cur * TILE;
+        const bool more = nxt < n_tiles;
+        const int32_t n2 = more ? grab(nxt) : n_tiles;  // its value is used at the end
+        // stage this tile's V rows in LDS: [position][d], padded rows, 16-byte writes;
+        // note whether any row of the tile sits behind an out-of-pool page entry
+        bool bad = false;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             u32x4 x = vr[v];
             if constexpr (CACHE == PAGED) {
                 if (!vok[v]) x = u32x4{0, 0, 0, 0};
+                bad = bad || !vok[v];
             }
             *reinterpret_cast<u32x4*>(vbuf + (v * PPI + l / CPR) * VROW + (l % CPR) * 16) = x;
         }
-        const bool more = tb + step < j1;
-        if (more) load_v(tb + step, vr);
+        if (more) load_v(j0 + nxt * TILE, vr);
 
         // S^T = K . Q^T
         f32x4 st[2][R];
@@ -267,18 +290,13 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
                     acc = mfma16x16x32<DT>(kc[tt][ks], qsm[(qt * KS + ks) * 64 + l], acc);
                 st[tt][qt] = acc;
             }
-        if (more) load_k(tb + step, kc);
+        if (more) load_k(j0 + nxt * TILE, kc);
 
         // Mask only where it can bite: a partial tile, rows that do not all see the
         // tile's last position (q_len > 1), the window mask, or (paged) a bad entry.
         bool edge = (tb + TILE > j1) ||
                     (p.q_len > 1 && (sink_window || span_pos(s, min(tb + TILE, j1) - 1) > P0));
-        if constexpr (CACHE == PAGED) {
-            bool bad = false;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) bad = bad || !vok[v];
-            edge = edge || __any(bad);
-        }
+        if constexpr (CACHE == PAGED) edge = edge || __any(bad);
         if (edge) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -368,77 +386,69 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             }
         }
         __builtin_amdgcn_wave_barrier();
+        cur = nxt;
+        nxt = n2;
     }
 
-    // ---- merge the four waves: per row (m, l), then sum of rescaled O in LDS
+    // ---- merge the four waves: each wave leaves its row sums and its unscaled O in
+    // a slot of LDS (one barrier), then every output element combines the four with
+    // the factors 2^(m_w - M), M = the largest of the four running maxima
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
         const float lt = xsum_16_32(lsum[qt]);
-        lsum[qt] = lt;
         if (lq == 0) {
             sm_m[wave][qt * 16 + lr] = m[qt];
             sm_l[wave][qt * 16 + lr] = lt;
         }
     }
-    __syncthreads();  // also: every wave is done with its V staging area
-    // per row: the workgroup's max M and sum L, and each wave's factor 2^(m_w - M)
-    if (tid < NQ) {
-        float M = NEG_INF;
+    __syncthreads();  // every wave is done with its V staging area
+    float* osum = reinterpret_cast<float*>(smem);  // [MFMA_WAVES][NQ][OROW]
+    {
+        float* slot = osum + wave * NQ * OROW;
 #pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, sm_m[w][tid]);
-        const float Mu = M == NEG_INF ? 0.0f : M;
-        float L = 0.0f;
+        for (int dt = 0; dt < DT16; ++dt)
 #pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) {
-            const float f = fast_exp2(sm_m[w][tid] - Mu);
-            sm_f[w][tid] = f;
-            L += sm_l[w][tid] * f;
-        }
-        sm_M[tid] = M;
-        sm_L[tid] = L;
+            for (int qt = 0; qt < R; ++qt) {
+                const f32x4 v = o[dt][qt];
+                *reinterpret_cast<float4*>(slot + (qt * 16 + lr) * OROW + dt * 16 + lq * 4) =
+                    float4{v[0], v[1], v[2], v[3]};
+            }
     }
     __syncthreads();
-    float* osum = reinterpret_cast<float*>(smem);  // [NQ][D]
-    for (int w = 0; w < MFMA_WAVES; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int dt = 0; dt < DT16; ++dt)
-#pragma unroll
-                for (int qt = 0; qt < R; ++qt) {
-                    const float f = sm_f[w][qt * 16 + lr];
-                    float4* dst =
-                        reinterpret_cast<float4*>(osum + (qt * 16 + lr) * D + dt * 16 + lq * 4);
-                    const f32x4 v = o[dt][qt] * f;
-                    if (w == 0) {
-                        *dst = float4{v[0], v[1], v[2], v[3]};
-                    } else {
-                        const float4 a = *dst;
-                        *dst = float4{a.x + v[0], a.y + v[1], a.z + v[2], a.w + v[3]};
-                    }
-                }
-        }
-        __syncthreads();
-    }
-    // rows out, four d at a time: the final rows (one split) or this split's partial
+    // rows out, four d at a time: the final rows (one piece) or this piece's partial
     for (int idx = tid; idx < NQ * D / 4; idx += MFMA_THREADS) {
         const int n = idx / (D / 4);
         const int d = (idx - n * (D / 4)) * 4;
         if (n >= p.rows) continue;
-        const float4 A = *reinterpret_cast<const float4*>(osum + n * D + d);
+        float M = NEG_INF;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, sm_m[w][n]);
+        const float Mu = M == NEG_INF ? 0.0f : M;
+        float L = 0.0f;
+        float4 A = float4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) {
+            const float f = fast_exp2(sm_m[w][n] - Mu);  // 0 for a wave that saw nothing
+            L += sm_l[w][n] * f;
+            const float4 a = *reinterpret_cast<const float4*>(osum + (w * NQ + n) * OROW + d);
+            A.x += f * a.x;
+            A.y += f * a.y;
+            A.z += f * a.z;
+            A.w += f * a.w;
+        }
         const int64_t rid = row_id_of(p, b, kvh, n);
         if (pc.nparts == 1) {
-            const float L = sm_L[n];
             const float inv = L > 0.0f ? 1.0f / L : 0.0f;
             const uint2 w = {pack2<DT>(A.x * inv, A.y * inv), pack2<DT>(A.z * inv, A.w * inv)};
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
         } else {
             const int64_t part = (pc.slot0 + pc.part) * NQ + n;
             store_partial4(p, part * D + d, A);
-            if (d == 0) store_partial_ml(p, part, sm_M[n], sm_L[n]);
+            if (d == 0) store_partial_ml(p, part, M, L);
         }
     }
     // the staging area is free again: the merge's scratch lives there
-    static_assert(sizeof(MergeSmem<NQ, MFMA_THREADS>) <= SMEM_V, "merge scratch");
+    static_assert(sizeof(MergeSmem<NQ, MFMA_THREADS>) <= SMEM, "merge scratch");
     __syncthreads();
     if (pc.nparts > 1) {
         auto& msm = *reinterpret_cast<MergeSmem<NQ, MFMA_THREADS>*>(smem);

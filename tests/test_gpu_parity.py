@@ -81,6 +81,37 @@ def test_q_zero_gives_mean_of_attended_values(name):
     gh.check(out, ref, case.dtype, f"{name}/q0")
 
 
+@pytest.mark.parametrize("q_len", [1, 5])
+def test_out_of_pool_page_entries_are_skipped(q_len):
+    """Page-table entries outside [0, num_blocks) are skipped (their positions are
+    dropped, nothing outside the pool is read).  With q = 0 every row is the mean of V
+    over the attended positions whose pages are valid.  q_len 1 runs the vector-ALU
+    kernel, q_len 5 (20 rows per KV head) the matrix-core one; the bad pages sit
+    mid-sequence, at a sequence start and in a short sequence."""
+    case = SMALL["paged_small"].replace(q_len=q_len)
+    print(f"case=paged_small q_len={q_len} out-of-pool entries", flush=True)
+    inp = workloads.make_inputs(case)
+    gh.poison_unattended(case, inp)
+    inp["q"].zero_()
+    bad = {(0, 3): -1, (0, 40): case.num_blocks + 3, (1, 0): -7, (1, 50): case.num_blocks,
+           (2, 1): 1 << 30}
+    bt_bad = inp["block_table"].clone()
+    for (b, page), v in bad.items():
+        bt_bad[b, page] = v
+    vflat = inp["v_cache"].reshape(-1, case.num_kv_heads, case.head_dim).double()
+    ref = np.zeros((case.batch, case.q_len, case.num_q_heads, case.head_dim))
+    for b in range(case.batch):
+        for i in range(case.q_len):
+            pos, slots = oracle.attended(case, inp["block_table"], inp["seq_lens"], b, i)
+            keep = [s for p_, s in zip(pos, slots) if (b, int(p_) // case.block_size) not in bad]
+            if keep:
+                mean = vflat[torch.as_tensor(keep)].mean(0).numpy()
+                ref[b, i] = np.repeat(mean, case.group, axis=0)
+    d = dict(gh.to_device(inp), block_table=bt_bad.cuda())
+    out = gh.run(case, d)
+    gh.check(out, ref, case.dtype, f"paged_small/q_len{q_len}/out-of-pool")
+
+
 def test_page_permutation_is_bit_identical():
     """The same logical sequences under two different page tables give the same bits."""
     case = SMALL["paged_small"]
