@@ -129,33 +129,112 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
     const int64_t dv = reinterpret_cast<const char*>(p.v) - reinterpret_cast<const char*>(p.k);
     const float c = p.scale_log2;
 
-    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
-    for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
-        const int b = pc.b;
-        const int kvh = pc.seg / p.row_blocks;
-        const int rb = pc.seg - kvh * p.row_blocks;
-        const int32_t n_tiles = (pc.jb - pc.ja + TWW - 1) / TWW;
-        if (tid == 0) s_next_tile = NWAVES;  // wave w starts with tile w
-        __syncthreads();
-
-        // Query rows of this KV head: row r = i * group + hg (new token i, head kvh*group+hg)
-        u32x4 qv[ROWS];
-        int row_i[ROWS];
+    // Per-piece view: sequence, KV head, row block, attended span, work range and
+    // the lane's K base address.
+    struct Ctx {
+        int b, kvh, rb;
+        int32_t ja, jb, n_tiles;
+        SeqSpan s;
+        const char* kb;
+    };
+    auto make_ctx = [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
+        Ctx x;
+        x.b = pc.b;
+        x.kvh = pc.seg / p.row_blocks;
+        x.rb = pc.seg - x.kvh * p.row_blocks;
+        x.ja = pc.ja;
+        x.jb = pc.jb;
+        x.n_tiles = (pc.jb - pc.ja + TWW - 1) / TWW;
+        x.s = s;
+        x.kb = reinterpret_cast<const char*>(p.k) + ((int64_t)x.kvh * p.stride_head + d0) * EB;
+        if constexpr (CACHE != PAGED) x.kb += (int64_t)x.b * p.stride_seq * EB;
+        return x;
+    };
+    // Query rows of a piece's KV head: row r = i * group + hg (new token i, head
+    // kvh*group + hg); row_i = -1 for padding rows.
+    auto load_q = [&](const Ctx& x, u32x4 (&qv)[ROWS]) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            const int rg = rb * ROWS + r;
+            const int rg = x.rb * ROWS + r;
             const bool ok = rg < p.rows;
             const int i = ok ? rg / p.group : 0;
-            const int h = kvh * p.group + (ok ? rg - i * p.group : 0);
-            row_i[r] = ok ? i : -1;
-            const int64_t rid = ((int64_t)b * p.q_len + i) * p.num_q_heads + h;
+            const int h = x.kvh * p.group + (ok ? rg - i * p.group : 0);
+            const int64_t rid = ((int64_t)x.b * p.q_len + i) * p.num_q_heads + h;
             qv[r] = ok ? load16(p.q, rid * D + d0, EB) : u32x4{0, 0, 0, 0};
         }
+    };
+
+    // Wave tile t of a piece covers work indices ja + t * TWW ...: lane group g of the
+    // wave takes ja + t * TWW + u * LGW + g (u < U), so each load instruction reads LGW
+    // consecutive positions.  Loads are branch-free: a lane past the piece (or behind a
+    // page-table entry outside the pool) loads a clamped, valid address and its data is
+    // discarded by selects (score -> -inf, V -> 0).
+    int32_t pos[U];
+    bool val[U];
+    const char* ka[U];
+    int32_t blk[U];  // paged: page-table entries of the tile to address next
+    auto fetch_pages = [&](const Ctx& x, int32_t t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = min(x.ja + t * TWW + u * LGW + lgw, x.jb - 1);
+            blk[u] = page_entry(p, x.b, span_pos(x.s, j));
+        }
+    };
+    auto address = [&](const Ctx& x, int32_t t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = x.ja + t * TWW + u * LGW + lgw;
+            val[u] = j < x.jb;
+            pos[u] = span_pos(x.s, min(j, x.jb - 1));
+            if constexpr (CACHE == PAGED) {
+                const bool in_pool = (uint32_t)blk[u] < (uint32_t)p.num_blocks;
+                val[u] = val[u] && in_pool;
+                const uint32_t unit = in_pool ? (uint32_t)blk[u] : 0u;
+                const uint32_t idx = (uint32_t)pos[u] & ((1u << p.log2_block) - 1);
+                ka[u] = x.kb + (uint64_t)unit * unit_bytes + idx * tok_bytes;
+            } else {
+                const Loc L = locate<CACHE>(p, x.s, x.b, pos[u]);
+                ka[u] = x.kb + (uint64_t)(uint32_t)L.idx * tok_bytes;
+            }
+        }
+    };
+    u32x4 kw[U], vw[U];
+    // Issue the loads of wave tile t of a piece (its Q rows too when `with_q`).
+    auto first_loads = [&](const Ctx& x, u32x4 (&qv)[ROWS]) __attribute__((always_inline)) {
+        load_q(x, qv);
+        if (wave < x.n_tiles) {
+            if constexpr (CACHE == PAGED) fetch_pages(x, wave);
+            address(x, wave);
+#pragma unroll
+            for (int u = 0; u < U; ++u) kw[u] = *reinterpret_cast<const u32x4*>(ka[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) vw[u] = *reinterpret_cast<const u32x4*>(ka[u] + dv);
+        }
+    };
+
+    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    // The next piece's Q rows and first wave tile are loaded before the current
+    // piece's epilogue (merge across waves, stores, arrival), so they are in flight
+    // while it runs.
+    bool preloaded = false;
+    u32x4 qv[ROWS];
+    for_each_piece_ahead(p, fp, ui, [&](const Piece& pc, const SeqSpan& s, bool has_next,
+                                       const Piece& npc, const SeqSpan& ns) __attribute__((always_inline)) {
+        const Ctx x = make_ctx(pc, s);
+        const int b = x.b, kvh = x.kvh, rb = x.rb;
+        const int32_t n_tiles = x.n_tiles;
+        if (tid == 0) s_next_tile = NWAVES;  // wave w starts with tile w
+        __syncthreads();
+        if (!preloaded) first_loads(x, qv);
+        preloaded = false;
+
         // MASKED: row r attends pos iff pos <= hi[r] and (pos < n_sink or pos >= lo[r])
         int32_t hi[ROWS], lo[ROWS];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            const int32_t P = s.T - p.q_len + (row_i[r] >= 0 ? row_i[r] : p.q_len - 1);
+            const int rg = rb * ROWS + r;
+            const int i = rg < p.rows ? rg / p.group : p.q_len - 1;
+            const int32_t P = s.T - p.q_len + i;
             hi[r] = P;
             lo[r] = p.mask_mode == MASK_SINK_WINDOW ? P - p.window + 1 : 0;
         }
@@ -168,43 +247,6 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             for (int e = 0; e < EPL; ++e) acc[r][e] = 0.0f;
         }
 
-        const char* kb = reinterpret_cast<const char*>(p.k) + ((int64_t)kvh * p.stride_head + d0) * EB;
-        if constexpr (CACHE != PAGED) kb += (int64_t)b * p.stride_seq * EB;
-
-        // Wave tile t covers work indices ja + t * TWW ...: lane group g of the wave
-        // takes ja + t * TWW + u * LGW + g (u < U), so each load instruction reads LGW
-        // consecutive positions.  Loads are branch-free: a lane past the piece (or
-        // behind a page-table entry outside the pool) loads a clamped, valid address
-        // and its data is discarded by selects (score -> -inf, V -> 0).
-        int32_t pos[U];
-        bool val[U];
-        const char* ka[U];
-        int32_t blk[U];  // paged: page-table entries of the tile to address next
-        auto fetch_pages = [&](int32_t t) __attribute__((always_inline)) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t j = min(pc.ja + t * TWW + u * LGW + lgw, pc.jb - 1);
-                blk[u] = page_entry(p, b, span_pos(s, j));
-            }
-        };
-        auto address = [&](int32_t t) __attribute__((always_inline)) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t j = pc.ja + t * TWW + u * LGW + lgw;
-                val[u] = j < pc.jb;
-                pos[u] = span_pos(s, min(j, pc.jb - 1));
-                if constexpr (CACHE == PAGED) {
-                    const bool in_pool = (uint32_t)blk[u] < (uint32_t)p.num_blocks;
-                    val[u] = val[u] && in_pool;
-                    const uint32_t unit = in_pool ? (uint32_t)blk[u] : 0u;
-                    const uint32_t idx = (uint32_t)pos[u] & ((1u << p.log2_block) - 1);
-                    ka[u] = kb + (uint64_t)unit * unit_bytes + idx * tok_bytes;
-                } else {
-                    const Loc L = locate<CACHE>(p, s, b, pos[u]);
-                    ka[u] = kb + (uint64_t)(uint32_t)L.idx * tok_bytes;
-                }
-            }
-        };
         int32_t cur = wave;
         // next tile for this wave: one LDS atomic per tile, issued a tile ahead
         // (deterministic mode: every NWAVES-th tile, a fixed summation order)
@@ -216,19 +258,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
                                            __HIP_MEMORY_SCOPE_WORKGROUP);
             return __builtin_amdgcn_readfirstlane(t);
         };
-
-        u32x4 kw[U], vw[U];
-        if (cur < n_tiles) {
-            if constexpr (CACHE == PAGED) fetch_pages(cur);
-            address(cur);
-#pragma unroll
-            for (int u = 0; u < U; ++u) kw[u] = *reinterpret_cast<const u32x4*>(ka[u]);
-#pragma unroll
-            for (int u = 0; u < U; ++u) vw[u] = *reinterpret_cast<const u32x4*>(ka[u] + dv);
-        }
         int32_t nxt = cur < n_tiles ? grab() : n_tiles;
         if constexpr (CACHE == PAGED) {
-            if (nxt < n_tiles) fetch_pages(nxt);
+            if (nxt < n_tiles) fetch_pages(x, nxt);
         }
         while (cur < n_tiles) {
             const bool more = nxt < n_tiles;
@@ -252,7 +284,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
 #pragma unroll
             for (int u = 0; u < U; ++u) vok[u] = val[u];
             if (more) {
-                address(nxt);
+                address(x, nxt);
 #pragma unroll
                 for (int u = 0; u < U; ++u) kw[u] = *reinterpret_cast<const u32x4*>(ka[u]);
             }
@@ -298,9 +330,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             if (cur < n_tiles) {
                 nxt = grab();
                 if constexpr (CACHE == PAGED) {
-                    if (nxt < n_tiles) fetch_pages(nxt);
+                    if (nxt < n_tiles) fetch_pages(x, nxt);
                 }
             }
+        }
+
+        if (has_next) {
+            first_loads(make_ctx(npc, ns), qv);
+            preloaded = true;
         }
 
         // Merge the lane groups of each wave (butterfly over lane offsets LPR .. 32).
@@ -390,8 +427,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
 // per-row mask); launches and occupancy queries go through the same choice.
 // Waves per workgroup (one workgroup per compute unit): as many as the register
 // budget of the row bucket allows.
+#ifndef KVATTN_VALU_WAVES_SMALL
+#define KVATTN_VALU_WAVES_SMALL 8   // 1 or 2 rows
+#endif
 constexpr int valu_waves(int rows_per_block) {
-    return rows_per_block <= 2 ? 12 : (rows_per_block <= 4 ? 8 : 4);
+    return rows_per_block <= 2 ? KVATTN_VALU_WAVES_SMALL : (rows_per_block <= 4 ? 8 : 4);
 }
 
 template <int DT, int D, int ROWS, int CACHE>

@@ -121,40 +121,64 @@ struct Piece {
     int part;       // this piece's index among them
 };
 
-// Calls f(piece, span) for each piece of unit u, in flat order.
+// Calls f(piece, span, has_next, next_piece, next_span) for each piece of unit u,
+// in flat order; the next piece of the unit (if any) is known while the current
+// one runs, so its first loads can be issued before the current one's epilogue.
 template <typename F>
-__device__ __forceinline__ void for_each_piece(const DecodeParams& p, const FlatPlan& fp,
-                                               int64_t u, F&& f) {
+__device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, const FlatPlan& fp,
+                                                     int64_t u, F&& f) {
     const int64_t x0 = u * fp.usz;
     const int64_t x1 = min(x0 + fp.usz, fp.total);
     const SeqAt at = seq_at(p, fp, x0);
     int b = at.b;
     int64_t off_b = at.off;
-    SeqSpan s = seq_span(p, b);
-    int64_t x = x0;
-    while (x < x1) {
-        const int64_t wb = (int64_t)s.count * p.segs_per_seq;
-        if (x >= off_b + wb) {  // past sequence b (or b holds nothing): next sequence
-            off_b += wb;
+    SeqSpan sb = seq_span(p, b);
+    // the piece that starts at flat index x (< x1)
+    auto piece_at = [&](int64_t x, Piece& pc, SeqSpan& ps) __attribute__((always_inline)) {
+        // sequences that hold nothing, or that x is already past, are skipped
+        while (x >= off_b + (int64_t)sb.count * p.segs_per_seq) {
+            off_b += (int64_t)sb.count * p.segs_per_seq;
             ++b;
-            s = seq_span(p, b);
-            continue;
+            sb = seq_span(p, b);
         }
-        Piece pc;
         pc.b = b;
-        pc.seg = (int)((x - off_b) / s.count);
-        const int64_t seg0 = off_b + (int64_t)pc.seg * s.count;
+        pc.seg = (int)((x - off_b) / sb.count);
+        const int64_t seg0 = off_b + (int64_t)pc.seg * sb.count;
         pc.ja = (int32_t)(x - seg0);
-        pc.jb = (int32_t)min<int64_t>(s.count, x1 - seg0);
+        pc.jb = (int32_t)min<int64_t>(sb.count, x1 - seg0);
         const int64_t first = seg0 / fp.usz;
-        const int64_t last = (seg0 + s.count - 1) / fp.usz;
+        const int64_t last = (seg0 + sb.count - 1) / fp.usz;
         pc.unit = (int64_t)b * p.segs_per_seq + pc.seg;
         pc.slot0 = first + pc.unit;
         pc.nparts = (int)(last - first + 1);
         pc.part = (int)(u - first);
-        f(pc, s);
-        x = seg0 + pc.jb;
+        ps = sb;
+        return seg0 + pc.jb;  // flat index just past the piece
+    };
+    if (x0 >= x1) return;
+    Piece cur;
+    SeqSpan cs;
+    int64_t x = piece_at(x0, cur, cs);
+    for (;;) {
+        Piece nx = cur;
+        SeqSpan ns = cs;
+        const bool more = x < x1;
+        const int64_t xn = more ? piece_at(x, nx, ns) : x;
+        f(cur, cs, more, nx, ns);
+        if (!more) break;
+        cur = nx;
+        cs = ns;
+        x = xn;
     }
+}
+
+// Calls f(piece, span) for each piece of unit u, in flat order.
+template <typename F>
+__device__ __forceinline__ void for_each_piece(const DecodeParams& p, const FlatPlan& fp,
+                                               int64_t u, F&& f) {
+    for_each_piece_ahead(p, fp, u,
+                         [&](const Piece& pc, const SeqSpan& s, bool, const Piece&,
+                             const SeqSpan&) __attribute__((always_inline)) { f(pc, s); });
 }
 
 // Runs body(u) for every unit this workgroup takes.  Workgroup w starts with unit
