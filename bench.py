@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_7b", choices=list(workloads.CONFIGS))
-    ap.add_argument("--layout", default="token_major", choices=["token_major", "head_major"])
+    ap.add_argument("--layout", default="head_major", choices=["token_major", "head_major"])
     ap.add_argument("--split-len", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="K/V copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
