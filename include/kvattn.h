@@ -147,13 +147,17 @@ KVATTN_API int kvattn_set_stream(kvattn_handle* h, void* stream);
 /* Batch for later decode calls, 0 .. max_batch (0 enqueues nothing). */
 KVATTN_API int kvattn_set_batch(kvattn_handle* h, int32_t batch);
 
-/* Force the number of attended positions per split-KV work item (a multiple of
- * 64, or 0 to let the library choose).  For tests of split-count invariance. */
+/* Force the length of the work units the step is cut into (attended positions of
+ * a (sequence, KV head) segment; a multiple of 64, or 0 to let the library choose).
+ * Every unit then has exactly this length (the last one of the step may be shorter),
+ * so segments are cut into many pieces.  For tests of split-count invariance. */
 KVATTN_API int kvattn_set_split_len(kvattn_handle* h, int32_t split_len);
 
-/* The decomposition a decode with these host arguments would use:
- * n_split work items per (sequence, KV head) of split_len positions each, and
- * the kernel family (0 = vector-ALU rows, 1 = matrix-core rows). */
+/* The decomposition a decode with these host arguments would use: n_split = the
+ * workgroups launched (one per compute unit for the automatic plan), split_len =
+ * the minimum unit length in positions (the exact unit length is placed on the
+ * device from seq_lens), and the kernel family (0 = vector-ALU rows, 1 =
+ * matrix-core rows). */
 KVATTN_API int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
                 int32_t window, int32_t* n_split, int32_t* split_len, int32_t* kernel);
 
