@@ -15,7 +15,12 @@ from __future__ import annotations
 
 from typing import Sequence
 
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+
+
+def kv_dtype(case) -> str:
+    """Element type of the caches (the case's kv_dtype, else its dtype)."""
+    return getattr(case, "kv_dtype", None) or case.dtype
 
 
 def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bytes_per_element: int) -> int:
@@ -53,15 +58,17 @@ def pages_touched(mask_mode: str, T: int, q_len: int, n_sink: int, window: int,
 
 def step_bytes(case, seq_lens: Sequence[int]) -> int:
     e = ELEM_BYTES[case.dtype]
+    ekv = ELEM_BYTES[kv_dtype(case)]
     total = 0
     for T in seq_lens:
         n = attended_count(case.mask_mode, int(T), case.q_len, case.n_sink, case.window)
-        total += 2 * n * case.num_kv_heads * case.head_dim * e
+        total += 2 * n * case.num_kv_heads * case.head_dim * ekv
         if case.cache_mode == "paged":
             total += 4 * pages_touched(case.mask_mode, int(T), case.q_len, case.n_sink,
                                        case.window, case.block_size)
     qo = case.batch * case.q_len * case.num_q_heads * case.head_dim * e
-    return total + 2 * qo + 4 * case.batch
+    scales = 2 * 4 * case.num_kv_heads if kv_dtype(case) == "fp8" else 0  # k_scale, v_scale
+    return total + 2 * qo + 4 * case.batch + scales
 
 
 def step_flops(case, seq_lens: Sequence[int]) -> int:

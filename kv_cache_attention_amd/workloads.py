@@ -20,7 +20,10 @@ Workload shapes follow the decode settings the source pages discuss:
 Draw order (fixed, so a seed names one input set): integer structure first
 (sequence lengths, block permutation), then Q, K, V as float32 standard
 normals, then the value scale (and the optional boost of K at position 0),
-then the cast to the storage dtype.
+then the cast to the storage dtype.  An 8-bit KV cache (kv_dtype "fp8", OCP
+E4M3) casts K and V per KV head: scale = max |x| / 448 over that head's slots
+(the largest finite E4M3 magnitude), code = round-to-nearest-even(x / scale);
+the scales (float32 [Hkv]) travel with the inputs as k_scale, v_scale.
 
 Layouts (row-major, head_dim innermost):
   q, out            [batch, q_len, num_q_heads, head_dim]
@@ -37,7 +40,9 @@ from typing import Optional, Tuple
 
 import torch
 
-DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "fp8": torch.float8_e4m3fn}
+E4M3_MAX = 448.0
 
 
 @dataclass(frozen=True)
@@ -61,6 +66,7 @@ class Case:
     seq_len_range: Optional[Tuple[int, int]] = None  # inclusive uniform integer range
     value_scale: float = 1.0
     k0_boost: float = 1.0           # K at logical position 0 multiplied by this
+    kv_dtype: Optional[str] = None  # cache element type when it differs from dtype ("fp8")
 
     @property
     def group(self) -> int:
@@ -98,7 +104,13 @@ PAGED_100K = Case("paged_100k", seed=5, batch=2, num_q_heads=32, num_kv_heads=8,
                   block_size=16, num_blocks=12500, seq_lens=(100000, 100000),
                   value_scale=0.5)
 
-CONFIGS = {c.name: c for c in (TINY, DECODE_7B, SPEC_VERIFY, SINK_WINDOW, PAGED_100K)}
+# The same shapes with an 8-bit (E4M3) K/V cache and per-KV-head scales.
+DECODE_7B_FP8 = DECODE_7B.replace(name="decode_7b_fp8", seed=6, kv_dtype="fp8")
+SINK_WINDOW_FP8 = SINK_WINDOW.replace(name="sink_window_fp8", seed=7, kv_dtype="fp8")
+PAGED_100K_FP8 = PAGED_100K.replace(name="paged_100k_fp8", seed=8, kv_dtype="fp8")
+
+CONFIGS = {c.name: c for c in (TINY, DECODE_7B, SPEC_VERIFY, SINK_WINDOW, PAGED_100K,
+                               DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8)}
 
 
 def cache_shape(case: Case) -> Tuple[int, ...]:
@@ -141,7 +153,8 @@ def make_inputs(case: Case, device: str = "cpu") -> dict:
         g = torch.Generator(device).manual_seed(case.seed)
     qshape = (case.batch, case.q_len, case.num_q_heads, case.head_dim)
     dt = DTYPES[case.dtype]
-    out = {}
+    kvdt = case.kv_dtype or case.dtype
+    out = {"k_scale": None, "v_scale": None}
     for name, shape in (("q", qshape), ("k_cache", cache_shape(case)), ("v_cache", cache_shape(case))):
         x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
         # 3. scale
@@ -158,12 +171,35 @@ def make_inputs(case: Case, device: str = "cpu") -> dict:
             else:
                 x[:, 0].mul_(case.k0_boost)
         # 4. cast
-        out[name] = x.to(dt) if dt != torch.float32 else x
+        if name != "q" and kvdt == "fp8":
+            # per KV head (dim 2 of every cache layout): scale = amax / 448
+            amax = x.abs().amax(dim=tuple(d for d in range(x.dim()) if d != 2))
+            sc = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).to(torch.float32)
+            out[name] = (x / sc.view(1, 1, -1, 1)).to(torch.float8_e4m3fn)
+            out["k_scale" if name == "k_cache" else "v_scale"] = sc
+        else:
+            out[name] = x.to(dt) if dt != torch.float32 else x
         del x
     out["seq_lens"] = seq_lens.to(device)
     out["block_table"] = block_table.to(device) if block_table is not None else None
     out["case"] = case
     return out
+
+
+def small_fp8_variants():
+    """Reduced cases with an 8-bit K/V cache: the reduced decode, ring and paged cases,
+    and a paged case with q_len 5 (per-row causal masks, 20 rows per KV head)."""
+    sv = small_variants()
+    return {
+        "decode_7b_small_fp8": sv["decode_7b_small"].replace(name="decode_7b_small_fp8",
+                                                             kv_dtype="fp8", seed=22),
+        "sink_window_small_fp8": sv["sink_window_small"].replace(name="sink_window_small_fp8",
+                                                                 kv_dtype="fp8", seed=24),
+        "paged_small_fp8": sv["paged_small"].replace(name="paged_small_fp8", kv_dtype="fp8",
+                                                     seed=25),
+        "paged_small_q5_fp8": sv["paged_small"].replace(name="paged_small_q5_fp8",
+                                                        kv_dtype="fp8", q_len=5, seed=26),
+    }
 
 
 def small_variants():

@@ -36,7 +36,13 @@
  *    positions to physical blocks).
  *
  * Storage formats are decoded from their bit definitions (IEEE binary16,
- * bfloat16 = the top half of binary32), exactly, into double.
+ * bfloat16 = the top half of binary32, OCP 8-bit E4M3), exactly, into double.
+ *
+ * An 8-bit KV cache (the FP8 KV-cache option the lesson lists among its serving
+ * flags, and KV quantisation in the StreamingLLM article's outlook) stores
+ * E4M3 codes; the pages fix no scaling, so the reading taken is the plainest
+ * one: one fp32 scale per KV head for K and one for V, the real value being
+ * code * scale.  The oracle dequantises (in double) and then runs unchanged.
  */
 #include <math.h>
 #include <stdint.h>
@@ -47,7 +53,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_FP8_E4M3 = 3 };
 enum { OR_CONTIGUOUS = 0, OR_PAGED = 1, OR_RING = 2 };
 enum { OR_CAUSAL = 0, OR_SINK_WINDOW = 1 };
 
@@ -74,10 +80,28 @@ static double bf16_to_f64(uint16_t b) {
     return (double)f;
 }
 
+/* OCP 8-bit E4M3 (the "FN" variant): 1 sign bit, 4 exponent bits (bias 7),
+ * 3 mantissa bits; exponent 0 is subnormal (m * 2^-9); no infinities, the codes
+ * S.1111.111 are NaN, so the largest finite magnitude is 1.75 * 2^8 = 448. */
+static double e4m3_to_f64(uint8_t c) {
+    int sign = c >> 7;
+    int e = (c >> 3) & 0xf;
+    int m = c & 0x7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);                  /* m/8 * 2^(1-7) */
+    else
+        v = ldexp((double)(m + 8), e - 10);        /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
 static double load_elem(const void* base, int dtype, int64_t idx) {
     switch (dtype) {
     case OR_F32: return (double)((const float*)base)[idx];
     case OR_F16: return f16_to_f64(((const uint16_t*)base)[idx]);
+    case OR_FP8_E4M3: return e4m3_to_f64(((const uint8_t*)base)[idx]);
     default: return bf16_to_f64(((const uint16_t*)base)[idx]);
     }
 }
@@ -140,6 +164,9 @@ typedef struct {
     int cache_mode, capacity, block_size, blocks_per_seq;
     int mask_mode, n_sink, window;
     double scale;                 /* 0 => 1/sqrt(head_dim) */
+    int kv_dtype;                 /* element type of the caches; dtype when equal */
+    const float* k_scale;         /* [num_kv_heads] dequantisation scales, or NULL (1) */
+    const float* v_scale;
 } oracle_problem;
 
 /* One output row: out[d] for (b, i, h).  Returns the number of attended
@@ -157,13 +184,16 @@ static int64_t decode_one_row(const oracle_problem* pr, const void* q, const voi
     for (int d = 0; d < D; ++d) out[d] = 0.0;
     if (n == 0) return 0;
     const int64_t qbase = (((int64_t)b * pr->q_len + i) * pr->num_q_heads + h) * D;
-    /* scores s_p = q . k_p * scale */
+    const int kvt = pr->kv_dtype;
+    const double ks = pr->k_scale ? (double)pr->k_scale[kvh] : 1.0;
+    const double vs = pr->v_scale ? (double)pr->v_scale[kvh] : 1.0;
+    /* scores s_p = q . k_p * scale, k_p dequantised */
     double m = -INFINITY;
     for (int64_t j = 0; j < n; ++j) {
         const int64_t kbase = (slots[j] * pr->num_kv_heads + kvh) * D;
         double s = 0.0;
         for (int d = 0; d < D; ++d)
-            s += load_elem(q, pr->dtype, qbase + d) * load_elem(kc, pr->dtype, kbase + d);
+            s += load_elem(q, pr->dtype, qbase + d) * (load_elem(kc, kvt, kbase + d) * ks);
         w[j] = s * scale;
         if (w[j] > m) m = w[j];
     }
@@ -177,7 +207,7 @@ static int64_t decode_one_row(const oracle_problem* pr, const void* q, const voi
     for (int64_t j = 0; j < n; ++j) {
         const double wj = w[j] / sum;
         const int64_t vbase = (slots[j] * pr->num_kv_heads + kvh) * D;
-        for (int d = 0; d < D; ++d) out[d] += wj * load_elem(vc, pr->dtype, vbase + d);
+        for (int d = 0; d < D; ++d) out[d] += wj * (load_elem(vc, kvt, vbase + d) * vs);
     }
     return n;
 }

@@ -30,7 +30,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 CACHE_CODES = {"contiguous": 0, "paged": 1, "ring": 2}
 MASK_CODES = {"causal": 0, "sink_window": 1}
 
@@ -43,7 +43,10 @@ class _Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "dtype", "batch", "num_q_heads", "num_kv_heads", "head_dim", "q_len",
         "cache_mode", "capacity", "block_size", "blocks_per_seq",
-        "mask_mode", "n_sink", "window")] + [("scale", ctypes.c_double)]
+        "mask_mode", "n_sink", "window")] + [("scale", ctypes.c_double),
+                                             ("kv_dtype", ctypes.c_int),
+                                             ("k_scale", ctypes.c_void_p),
+                                             ("v_scale", ctypes.c_void_p)]
 
 
 def load():
@@ -77,11 +80,23 @@ def threads() -> int:
     return load().oracle_max_threads()
 
 
-def _problem(pr, scale: float = 0.0) -> _Problem:
+def kv_dtype_of(pr) -> str:
+    """Element type of the caches: the problem's kv_dtype when it has one, else dtype."""
+    return getattr(pr, "kv_dtype", None) or pr.dtype
+
+
+def _problem(pr, scale: float = 0.0, k_scale=None, v_scale=None) -> _Problem:
+    # k_scale / v_scale: float32 CPU tensors [num_kv_heads] kept alive by the caller
     return _Problem(DTYPE_CODES[pr.dtype], pr.batch, pr.num_q_heads, pr.num_kv_heads,
                     pr.head_dim, pr.q_len, CACHE_CODES[pr.cache_mode], pr.capacity,
                     pr.block_size, pr.capacity // pr.block_size, MASK_CODES[pr.mask_mode],
-                    pr.n_sink, pr.window, float(scale))
+                    pr.n_sink, pr.window, float(scale), DTYPE_CODES[kv_dtype_of(pr)],
+                    _ptr(k_scale), _ptr(v_scale))
+
+
+def _scales(k_scale, v_scale):
+    f = lambda t: None if t is None else _cpu(t).to(torch.float32).contiguous()
+    return f(k_scale), f(v_scale)
 
 
 def _cpu(t: Optional[torch.Tensor]):
@@ -101,12 +116,14 @@ def _ptr(t, ctype=None):
 
 
 def decode(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0,
-           n_threads: int = 0) -> np.ndarray:
-    """All rows; float64 [batch, q_len, num_q_heads, head_dim]."""
+           n_threads: int = 0, k_scale=None, v_scale=None) -> np.ndarray:
+    """All rows; float64 [batch, q_len, num_q_heads, head_dim].  An 8-bit cache
+    (pr.kv_dtype == "fp8") takes per-KV-head dequantisation scales k_scale, v_scale."""
     lib = load()
     q, kc, vc, bt, sl = (_cpu(x) for x in (q, k_cache, v_cache, block_table, seq_lens))
+    ks, vs = _scales(k_scale, v_scale)
     out = np.zeros((pr.batch, pr.q_len, pr.num_q_heads, pr.head_dim), np.float64)
-    rc = lib.oracle_decode(ctypes.byref(_problem(pr, scale)), _ptr(q), _ptr(kc), _ptr(vc),
+    rc = lib.oracle_decode(ctypes.byref(_problem(pr, scale, ks, vs)), _ptr(q), _ptr(kc), _ptr(vc),
                            _ptr(bt, ctypes.c_int32), _ptr(sl, ctypes.c_int32),
                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), n_threads)
     if rc != 0:
@@ -115,13 +132,14 @@ def decode(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0,
 
 
 def decode_rows(pr, q, k_cache, v_cache, block_table, seq_lens, rows, scale: float = 0.0,
-                n_threads: int = 0) -> np.ndarray:
+                n_threads: int = 0, k_scale=None, v_scale=None) -> np.ndarray:
     """Listed rows only: rows is int [n, 3] of (b, i, h); returns float64 [n, head_dim]."""
     lib = load()
     q, kc, vc, bt, sl = (_cpu(x) for x in (q, k_cache, v_cache, block_table, seq_lens))
+    ks, vs = _scales(k_scale, v_scale)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
     out = np.zeros((rows.shape[0], pr.head_dim), np.float64)
-    rc = lib.oracle_decode_rows(ctypes.byref(_problem(pr, scale)), _ptr(q), _ptr(kc), _ptr(vc),
+    rc = lib.oracle_decode_rows(ctypes.byref(_problem(pr, scale, ks, vs)), _ptr(q), _ptr(kc), _ptr(vc),
                                 _ptr(bt, ctypes.c_int32), _ptr(sl, ctypes.c_int32),
                                 rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                 rows.shape[0],
@@ -154,7 +172,8 @@ def attended(pr, block_table, seq_lens, b: int, i: int):
 # ---------------------------------------------------------------------------
 
 def to_f64(t) -> np.ndarray:
-    """Exact upcast of a stored tensor (f32 / f16 / bf16) to float64 (torch's conversion)."""
+    """Exact upcast of a stored tensor (f32 / f16 / bf16 / float8_e4m3fn) to float64
+    (torch's conversion)."""
     if isinstance(t, np.ndarray):
         return t.astype(np.float64)
     return t.detach().cpu().to(torch.float64).numpy()
@@ -185,12 +204,16 @@ def slot_np(cache_mode: str, b: int, p: np.ndarray, capacity: int, block_size: i
     return b * capacity + np.where(p < n_sink, p, n_sink + (p - n_sink) % max(r, 1))
 
 
-def decode_np(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0) -> np.ndarray:
-    """float64 [batch, q_len, Hq, D]; gathers only the attended slots."""
+def decode_np(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0,
+              k_scale=None, v_scale=None) -> np.ndarray:
+    """float64 [batch, q_len, Hq, D]; gathers only the attended slots.  8-bit caches
+    are dequantised with the per-KV-head scales (torch's E4M3 conversion)."""
     D, Hq, Hkv = pr.head_dim, pr.num_q_heads, pr.num_kv_heads
     g = Hq // Hkv
     sc = scale if scale != 0.0 else 1.0 / math.sqrt(D)
     q64 = to_f64(q)
+    ks = np.ones(Hkv) if k_scale is None else to_f64(k_scale.float())
+    vs = np.ones(Hkv) if v_scale is None else to_f64(v_scale.float())
     kflat = k_cache.reshape(-1, Hkv, D)
     vflat = v_cache.reshape(-1, Hkv, D)
     sl = np.asarray(seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens)
@@ -205,8 +228,8 @@ def decode_np(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0
             slots = slot_np(pr.cache_mode, b, pos, pr.capacity, pr.block_size, block_table,
                             pr.n_sink)
             idx = torch.as_tensor(slots)
-            K = to_f64(kflat.index_select(0, idx.to(kflat.device)))[:, kv_of_h, :]  # [n, Hq, D]
-            V = to_f64(vflat.index_select(0, idx.to(vflat.device)))[:, kv_of_h, :]
+            K = (to_f64(kflat.index_select(0, idx.to(kflat.device))) * ks[None, :, None])[:, kv_of_h, :]
+            V = (to_f64(vflat.index_select(0, idx.to(vflat.device))) * vs[None, :, None])[:, kv_of_h, :]
             s = np.einsum("nhd,hd->hn", K, q64[b, i]) * sc
             w = np.exp(s - s.max(axis=1, keepdims=True))
             w /= w.sum(axis=1, keepdims=True)

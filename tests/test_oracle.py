@@ -51,6 +51,26 @@ def test_bf16_decode_exhaustive(oracle_lib):
     assert np.array_equal(ref[~nan], got[~nan])
 
 
+def test_e4m3_decode_exhaustive(oracle_lib):
+    """8-bit caches: the C oracle's E4M3 decoder (written from the format's bit
+    definition) agrees with torch's float8_e4m3fn conversion on all 256 codes, and with
+    the values that define the OCP E4M3 format: largest finite magnitude 448 (0x7E),
+    smallest normal 2^-6 (0x08), smallest subnormal 2^-9 (0x01), 1.0 = 0x38, NaN for
+    S.1111.111 and no infinities."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).contiguous()
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle_lib.oracle_decode_elem(codes.data_ptr(), 3, i) for i in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    spot = {0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+            0x38: 1.0, 0x00: 0.0, 0x3F: 1.875, 0x40: 2.0}
+    for c, v in spot.items():
+        assert got[c] == v, hex(c)
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.isfinite(got[[c for c in range(256) if c & 0x7F != 0x7F]]).all()
+
+
 # --------------------------------------------------------------------------- closed forms
 
 def test_kv_bytes_golden():
@@ -439,6 +459,46 @@ def test_c_oracle_equals_numpy_twin(name):
     b = oracle.decode_np(*args)
     assert np.isfinite(a).all()
     assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("name", list(workloads.small_fp8_variants()))
+def test_fp8_cache_c_oracle_equals_dequantized_twin(name):
+    """8-bit caches: the C oracle (bit-definition decoder, dequantise, attend) and the
+    NumPy twin (torch's E4M3 conversion times the per-head scales) agree."""
+    case = workloads.small_fp8_variants()[name]
+    inp = workloads.make_inputs(case)
+    args = (case, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["seq_lens"])
+    kw = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    a = oracle.decode(*args, **kw)
+    b = oracle.decode_np(*args, **kw)
+    assert np.isfinite(a).all()
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_fp8_scales_enter_k_and_v_where_the_definition_puts_them():
+    """k = code * k_scale and v = code * v_scale, per KV head: doubling one head's
+    k_scale while halving its query rows leaves the output unchanged; multiplying its
+    v_scale by 4 multiplies exactly that head's output rows by 4; the other heads do
+    not move."""
+    case = workloads.small_fp8_variants()["paged_small_fp8"]
+    inp = workloads.make_inputs(case)
+    ks, vs = inp["k_scale"].clone(), inp["v_scale"].clone()
+    base = oracle.decode(case, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
+                         inp["seq_lens"], k_scale=ks, v_scale=vs)
+    g = case.group
+    q2 = inp["q"].clone()
+    q2[:, :, 0:g] *= 0.5                          # query heads of KV head 0
+    ks2 = ks.clone()
+    ks2[0] *= 2.0
+    a = oracle.decode(case, q2, inp["k_cache"], inp["v_cache"], inp["block_table"],
+                      inp["seq_lens"], k_scale=ks2, v_scale=vs)
+    assert np.allclose(a, base, rtol=1e-12, atol=1e-14)
+    vs3 = vs.clone()
+    vs3[1] *= 4.0  # a power of two: exact in float32
+    b = oracle.decode(case, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
+                      inp["seq_lens"], k_scale=ks, v_scale=vs3)
+    assert np.allclose(b[:, :, g:2 * g], 4.0 * base[:, :, g:2 * g], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(b[:, :, 0:g], base[:, :, 0:g])
 
 
 @pytest.mark.parametrize("name", list(workloads.CONFIGS))
