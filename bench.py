@@ -91,7 +91,8 @@ def cpu_baseline(case, d, out, n_rows, step_bytes):
     sl = d["seq_lens"].cpu()
     threads = oracle.threads()
     t0 = time.perf_counter()
-    ref = oracle.decode_rows(case, q, kc, vc, bt, sl, rows)
+    ref = oracle.decode_rows(case, q, kc, vc, bt, sl, rows, k_scale=d["k_scale"],
+                             v_scale=d["v_scale"])
     dt = time.perf_counter() - t0
     # the sample's share of the step's algorithmic bytes, so the rate is in the metric's unit
     byts = step_bytes * len(rows) / total
@@ -136,6 +137,8 @@ def main():
     h = kb.KVAttn.for_case(case, layout=a.layout)
     if a.split_len:
         h.set_split_len(a.split_len)
+    if getattr(case, "kv_dtype", None) == "fp8":
+        h.set_kv_scales(d["k_scale"], d["v_scale"])
     n_split, split_len, kernel = h.plan(case.q_len, case.mask_mode, case.n_sink, case.window)
     stream = torch.cuda.Stream(dev)   # default priority
     out = torch.empty_like(d["q"])
@@ -187,7 +190,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.dtype,
+        "dtype": case.dtype if not getattr(case, "kv_dtype", None) else
+                 f"{case.dtype} (K/V {case.kv_dtype} e4m3)",
         "data": "synthetic (seeded N(0,1) x scale, device generator)",
         "config": {
             "workload": case.name, "batch": case.batch, "num_q_heads": case.num_q_heads,
@@ -234,7 +238,7 @@ def default_cpu_rows(case):
     # about 10-30 s of single-threaded-equivalent oracle work on a few host cores
     per_row = {"tiny": 4, "decode_7b": 512, "spec_verify": 320, "sink_window": 128,
                "paged_100k": 64}
-    return per_row.get(case.name, 64)
+    return per_row.get(case.name.replace("_fp8", ""), 64)
 
 
 def out_for_copy0(h, d, kcs, vcs, case, mask):

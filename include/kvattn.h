@@ -28,7 +28,8 @@
  *                            or p >= P - window + 1 (the `window` most recent
  *                            positions, its own included).
  *
- * Layouts (row-major, head_dim innermost and contiguous; element type = dtype):
+ * Layouts (row-major, head_dim innermost and contiguous; element type = dtype, or
+ * kv_dtype for the caches):
  *   q, out       [batch, q_len, num_q_heads, head_dim]
  *   CONTIGUOUS and RING caches
  *                token-major (default): [batch, capacity, num_kv_heads, head_dim]
@@ -81,7 +82,7 @@ enum kvattn_status {
     KVATTN_ERR_HIP = -4            /* a HIP runtime call failed (text in kvattn_last_error) */
 };
 
-enum kvattn_dtype { KVATTN_F32 = 0, KVATTN_F16 = 1, KVATTN_BF16 = 2 };
+enum kvattn_dtype { KVATTN_F32 = 0, KVATTN_F16 = 1, KVATTN_BF16 = 2, KVATTN_FP8_E4M3 = 3 };
 enum kvattn_cache_mode { KVATTN_CONTIGUOUS = 0, KVATTN_PAGED = 1, KVATTN_RING = 2 };
 enum kvattn_mask_mode { KVATTN_MASK_CAUSAL = 0, KVATTN_MASK_SINK_WINDOW = 1 };
 enum kvattn_layout { KVATTN_LAYOUT_TOKEN_MAJOR = 0, KVATTN_LAYOUT_HEAD_MAJOR = 1 };
@@ -101,6 +102,10 @@ typedef struct kvattn_config {
     int32_t layout;         /* kvattn_layout */
     float scale;            /* 0 => 1 / sqrt(head_dim) */
     uint32_t flags;         /* KVATTN_FLAG_* bits, 0 for the defaults */
+    int32_t kv_dtype;       /* element type of both caches: 0 or dtype = the same as q;
+                               KVATTN_FP8_E4M3 (q F16 or BF16) = 8-bit OCP E4M3 codes, the
+                               real value being code * the KV head's scale
+                               (kvattn_set_kv_scales) */
 } kvattn_config;
 
 /* Flags.
@@ -146,6 +151,12 @@ KVATTN_API int kvattn_set_stream(kvattn_handle* h, void* stream);
 
 /* Batch for later decode calls, 0 .. max_batch (0 enqueues nothing). */
 KVATTN_API int kvattn_set_batch(kvattn_handle* h, int32_t batch);
+
+/* Dequantisation scales of an 8-bit cache (kv_dtype KVATTN_FP8_E4M3): float32
+ * [num_kv_heads] device arrays for K and V, read by later decode calls (borrowed:
+ * they must stay valid while those calls are in flight).  Scales must be positive
+ * and finite.  Required before decoding an 8-bit cache; ignored otherwise. */
+KVATTN_API int kvattn_set_kv_scales(kvattn_handle* h, const float* k_scale, const float* v_scale);
 
 /* Force the length of the work units the step is cut into (attended positions of
  * a (sequence, KV head) segment; a multiple of 64, or 0 to let the library choose).

@@ -18,22 +18,23 @@ LIB_PATH = os.path.join(_HERE, "libkvattn.so")
 
 KVATTN_OK = 0
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "CAPACITY", -4: "HIP"}
-DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
-TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8": torch.float8_e4m3fn}
 CACHE = {"contiguous": 0, "paged": 1, "ring": 2}
 MASK = {"causal": 0, "sink_window": 1}
 LAYOUT = {"token_major": 0, "head_major": 1}
 
 EXPORTS = ("kvattn_create", "kvattn_decode", "kvattn_destroy", "kvattn_set_stream",
-           "kvattn_set_batch", "kvattn_set_split_len", "kvattn_plan", "kvattn_workspace_bytes",
-           "kvattn_last_error", "kvattn_debug_gather")
+           "kvattn_set_batch", "kvattn_set_split_len", "kvattn_set_kv_scales", "kvattn_plan",
+           "kvattn_workspace_bytes", "kvattn_last_error", "kvattn_debug_gather")
 
 
 class kvattn_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "dtype", "num_q_heads", "num_kv_heads", "head_dim", "max_batch", "max_q_len",
         "cache_mode", "capacity", "block_size", "num_blocks", "layout")] + [
-        ("scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+        ("scale", ctypes.c_float), ("flags", ctypes.c_uint32), ("kv_dtype", ctypes.c_int32)]
 
 
 FLAG_DETERMINISTIC = 1
@@ -70,6 +71,8 @@ def load() -> ctypes.CDLL:
     lib.kvattn_set_batch.restype = ctypes.c_int
     lib.kvattn_set_split_len.argtypes = [H, i32]
     lib.kvattn_set_split_len.restype = ctypes.c_int
+    lib.kvattn_set_kv_scales.argtypes = [H, vp, vp]
+    lib.kvattn_set_kv_scales.restype = ctypes.c_int
     lib.kvattn_plan.argtypes = [H, i32, i32, i32, i32, i32p, i32p, i32p]
     lib.kvattn_plan.restype = ctypes.c_int
     lib.kvattn_workspace_bytes.argtypes = [ctypes.POINTER(kvattn_config),
@@ -101,10 +104,12 @@ def _dev_ptr(t: Optional[torch.Tensor], name: str):
 def make_config(*, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
                 max_batch: int, max_q_len: int, cache_mode: str, capacity: int,
                 block_size: int = 16, num_blocks: int = 0, layout: str = "token_major",
-                scale: float = 0.0, deterministic: bool = False) -> kvattn_config:
+                scale: float = 0.0, deterministic: bool = False,
+                kv_dtype: Optional[str] = None) -> kvattn_config:
     return kvattn_config(DTYPE[dtype], num_q_heads, num_kv_heads, head_dim, max_batch, max_q_len,
                          CACHE[cache_mode], capacity, block_size, num_blocks, LAYOUT[layout],
-                         scale, FLAG_DETERMINISTIC if deterministic else 0)
+                         scale, FLAG_DETERMINISTIC if deterministic else 0,
+                         DTYPE[kv_dtype] if kv_dtype else 0)
 
 
 # ------------------------------------------------------------ same names as the C ABI
@@ -137,6 +142,16 @@ def kvattn_set_batch(h, batch: int) -> None:
 
 def kvattn_set_split_len(h, split_len: int) -> None:
     _check(load().kvattn_set_split_len(h, split_len), "kvattn_set_split_len")
+
+
+def kvattn_set_kv_scales(h, k_scale, v_scale) -> None:
+    if k_scale is None or v_scale is None:
+        raise ValueError("k_scale and v_scale are required")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    _check(load().kvattn_set_kv_scales(h, _dev_ptr(k_scale, "k_scale"), _dev_ptr(v_scale, "v_scale")),
+           "kvattn_set_kv_scales")
 
 
 def kvattn_plan(h, q_len: int, mask_mode: int, n_sink: int, window: int):
@@ -173,13 +188,16 @@ class KVAttn:
     def __init__(self, *, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  max_batch: int, max_q_len: int, cache_mode: str, capacity: int,
                  block_size: int = 16, num_blocks: int = 0, layout: str = "token_major",
-                 scale: float = 0.0, deterministic: bool = False):
+                 scale: float = 0.0, deterministic: bool = False,
+                 kv_dtype: Optional[str] = None):
         self.cfg = make_config(dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                                head_dim=head_dim, max_batch=max_batch, max_q_len=max_q_len,
                                cache_mode=cache_mode, capacity=capacity, block_size=block_size,
                                num_blocks=num_blocks, layout=layout, scale=scale,
-                               deterministic=deterministic)
+                               deterministic=deterministic, kv_dtype=kv_dtype)
         self.dtype = dtype
+        self.kv_dtype = kv_dtype or dtype
+        self._scales = None  # keeps the scale tensors alive while the handle reads them
         self.h = kvattn_create(self.cfg)
 
     @classmethod
@@ -190,7 +208,7 @@ class KVAttn:
                    max_batch=max_batch or case.batch, max_q_len=max_q_len or case.q_len,
                    cache_mode=case.cache_mode, capacity=case.capacity,
                    block_size=case.block_size, num_blocks=case.num_blocks, layout=layout,
-                   deterministic=deterministic)
+                   deterministic=deterministic, kv_dtype=getattr(case, "kv_dtype", None))
 
     def close(self) -> None:
         if self.h:
@@ -209,14 +227,19 @@ class KVAttn:
     def set_split_len(self, split_len: int) -> None:
         kvattn_set_split_len(self.h, split_len)
 
+    def set_kv_scales(self, k_scale, v_scale) -> None:
+        kvattn_set_kv_scales(self.h, k_scale, v_scale)
+        self._scales = (k_scale, v_scale)
+
     def plan(self, q_len: int, mask_mode: str = "causal", n_sink: int = 0, window: int = 0):
         return kvattn_plan(self.h, q_len, MASK[mask_mode], n_sink, window)
 
     def decode(self, q, k_cache, v_cache, block_table, seq_lens, q_len: int,
                mask_mode: str = "causal", n_sink: int = 0, window: int = 0, out=None,
                stream: Optional[torch.cuda.Stream] = None):
-        want = TORCH_DTYPE[self.dtype]
-        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        for name, t, want in (("q", q, TORCH_DTYPE[self.dtype]),
+                              ("k_cache", k_cache, TORCH_DTYPE[self.kv_dtype]),
+                              ("v_cache", v_cache, TORCH_DTYPE[self.kv_dtype])):
             if t.dtype != want:
                 raise ValueError(f"{name} must be {want}")
         if seq_lens.dtype != torch.int32 or (block_table is not None and

@@ -15,7 +15,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvattn.cpp", "decode_valu.hip", "decode_mfma.hip", "debug_gather.hip"]
+SOURCES = ["kvattn.cpp", "decode_valu.hip", "valu_f16.hip", "valu_bf16.hip", "valu_f32.hip",
+           "valu_f16_fp8.hip", "valu_bf16_fp8.hip", "decode_mfma.hip", "debug_gather.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -9,7 +9,7 @@
 
 namespace kvattn {
 
-enum : int { F32 = 0, F16 = 1, BF16 = 2 };
+enum : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };  // FP8: OCP E4M3 codes
 enum : int { CONTIGUOUS = 0, PAGED = 1, RING = 2 };
 enum : int { MASK_CAUSAL = 0, MASK_SINK_WINDOW = 1 };
 
@@ -37,6 +37,8 @@ struct DecodeParams {
     int32_t min_chunk;    // smallest unit (positions)
     int32_t units_per_wg; // units per workgroup the flat range is cut into
     int32_t deterministic;  // waves take fixed tiles instead of a shared queue
+    const float* k_scale; // 8-bit caches: [Hkv] dequantisation scales (else NULL)
+    const float* v_scale;
     float scale_log2;     // softmax scale * log2(e): scores are kept in the exp2 domain
 };
 
@@ -167,6 +169,7 @@ template <int DT> struct Elem;
 template <> struct Elem<F32> { static constexpr int bytes = 4; };
 template <> struct Elem<F16> { static constexpr int bytes = 2; };
 template <> struct Elem<BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<FP8> { static constexpr int bytes = 1; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -189,16 +192,17 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 
 // ---------------------------------------------------------------- cross-lane sums
 
-// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of the group
+// Sum over aligned groups of N lanes (N = 4, 8, 16 or 32); every lane of the group
 // receives the same value.  Steps pair lanes with commutative adds, so all lanes
 // hold bit-identical results.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(N == 8 || N == 16 || N == 32, "group size");
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
     // quad_perm [1,0,3,2]: swap neighbours
     x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, false);
     // quad_perm [2,3,0,1]: swap pairs
     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, false);
+    if constexpr (N == 4) return x;
     // row_half_mirror: lane i <-> 7 - i within each 8
     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, false);
     if constexpr (N >= 16) {

@@ -60,6 +60,8 @@ struct kvattn_handle {
     hipStream_t stream;
     int32_t batch;
     int32_t forced_chunk;
+    const float* k_scale;   // 8-bit caches: per-KV-head dequantisation scales (device)
+    const float* v_scale;
     float* ws;              // partials: acc [ws_floats], (m, l), then the arrival counters
     int64_t ws_part_rows;   // partial rows (slot x segment row) the workspace holds
     int64_t n_units;        // arrival counters (batch x segments per sequence)
@@ -82,8 +84,11 @@ int64_t max_attended(const kvattn_config& c, int q_len, int mask_mode, int n_sin
     return cap;
 }
 
+// Element type of the caches (the config's kv_dtype, 0 meaning the same as dtype).
+int kv_dtype_of(const kvattn_config& c) { return c.kv_dtype == 0 ? c.dtype : c.kv_dtype; }
+
 bool use_mfma(const kvattn_config& c, int q_len) {
-    return kvattn::mfma_supported(c.dtype, c.head_dim, rows_of(c, q_len));
+    return kv_dtype_of(c) == c.dtype && kvattn::mfma_supported(c.dtype, c.head_dim, rows_of(c, q_len));
 }
 
 int row_blocks_of(const kvattn_config& c, int q_len) {
@@ -127,6 +132,10 @@ int validate_config(const kvattn_config* c) {
     if (c->capacity < 1) return fail(KVATTN_ERR_INVALID_ARG, "capacity must be >= 1");
     if (c->layout != KVATTN_LAYOUT_TOKEN_MAJOR && c->layout != KVATTN_LAYOUT_HEAD_MAJOR)
         return fail(KVATTN_ERR_INVALID_ARG, "unknown layout");
+    if (c->kv_dtype != 0 && c->kv_dtype != c->dtype && c->kv_dtype != KVATTN_FP8_E4M3)
+        return fail(KVATTN_ERR_UNSUPPORTED, "kv_dtype must be 0, dtype or FP8_E4M3");
+    if (c->kv_dtype == KVATTN_FP8_E4M3 && c->dtype != KVATTN_F16 && c->dtype != KVATTN_BF16)
+        return fail(KVATTN_ERR_UNSUPPORTED, "8-bit caches need F16 or BF16 queries");
     if (c->flags & ~KVATTN_FLAG_DETERMINISTIC)
         return fail(KVATTN_ERR_INVALID_ARG, "unknown flag bits");
     if (!(c->scale >= 0.0f) || std::isinf(c->scale))
@@ -179,8 +188,8 @@ int resident_for(const kvattn_config& c, int q_len, int num_cus) {
     const int rows = rows_of(c, q_len);
     const bool mfma = use_mfma(c, q_len);
     const void* k = mfma ? kvattn::select_mfma_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
-                         : kvattn::select_valu_kernel(c.dtype, c.head_dim, rows, c.cache_mode,
-                                                      q_len > 1);
+                         : kvattn::select_valu_kernel(c.dtype, kv_dtype_of(c), c.head_dim, rows,
+                                                      c.cache_mode, q_len > 1);
     int per_cu = 0;
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(
                   &per_cu, k, mfma ? kvattn::kMfmaThreads : kvattn::valu_threads(rows), 0) != hipSuccess ||
@@ -268,6 +277,8 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
     h->stream = nullptr;
     h->batch = cfg->max_batch;
     h->forced_chunk = 0;
+    h->k_scale = nullptr;
+    h->v_scale = nullptr;
     const int64_t D = cfg->head_dim, H = cfg->num_kv_heads;
     const int64_t unit = cfg->cache_mode == KVATTN_PAGED ? cfg->block_size : cfg->capacity;
     if (cfg->layout == KVATTN_LAYOUT_TOKEN_MAJOR) {
@@ -331,6 +342,14 @@ int kvattn_set_batch(kvattn_handle* h, int32_t batch) {
     return KVATTN_OK;
 }
 
+int kvattn_set_kv_scales(kvattn_handle* h, const float* k_scale, const float* v_scale) {
+    if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
+    if (!k_scale || !v_scale) return fail(KVATTN_ERR_INVALID_ARG, "scales must be non-NULL");
+    h->k_scale = k_scale;
+    h->v_scale = v_scale;
+    return KVATTN_OK;
+}
+
 int kvattn_set_split_len(kvattn_handle* h, int32_t split_len) {
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
     if (split_len < 0 || split_len % kChunkQuantum)
@@ -391,6 +410,8 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.min_chunk = min_chunk;
     p.units_per_wg = h->forced_chunk > 0 ? 1 << 30 : kUnitsPerWg;  // forced: units of exactly min_chunk
     p.deterministic = (c.flags & KVATTN_FLAG_DETERMINISTIC) ? 1 : 0;
+    p.k_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->k_scale : nullptr;
+    p.v_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->v_scale : nullptr;
     const float scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
 }
@@ -408,6 +429,8 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
         return fail(KVATTN_ERR_INVALID_ARG, "block_table must be given exactly for a paged cache");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return fail(KVATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
+    if (kv_dtype_of(h->cfg) == KVATTN_FP8_E4M3 && (!h->k_scale || !h->v_scale))
+        return fail(KVATTN_ERR_INVALID_ARG, "an 8-bit cache needs kvattn_set_kv_scales first");
     int grid, chunk;
     rc = plan_for(h, q_len, mask_mode, n_sink, window, &grid, &chunk);
     if (rc) return rc;
@@ -417,7 +440,8 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
     hipError_t e =
         use_mfma(h->cfg, q_len)
             ? kvattn::launch_decode_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
-            : kvattn::launch_decode_valu(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream);
+            : kvattn::launch_decode_valu(p, h->cfg.dtype, kv_dtype_of(h->cfg), h->cfg.head_dim,
+                                         grid, h->stream);
     if (e != hipSuccess)
         return fail(KVATTN_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return KVATTN_OK;

@@ -9,11 +9,13 @@ namespace kvattn {
 
 // Vector-ALU split-KV kernel (any row count; rows above 16 run in blocks of 16).
 // `grid` workgroups share the step's work in equal slices.
-hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int head_dim, int grid,
-                              hipStream_t st);
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int kv_dtype, int head_dim,
+                              int grid, hipStream_t st);
 int valu_rows_per_block(int rows);
 int valu_threads(int rows);  // workgroup size of the instance serving `rows`
-const void* select_valu_kernel(int dtype, int head_dim, int rows, int cache_mode, bool masked);
+// kv_dtype: element type of the caches (FP8 = 8-bit E4M3 codes, with F16/BF16 queries)
+const void* select_valu_kernel(int dtype, int kv_dtype, int head_dim, int rows, int cache_mode,
+                               bool masked);
 
 // Matrix-core split-KV kernel for 16 to 64 rows per KV head (f16 / bf16).
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,

@@ -33,7 +33,10 @@ def poison_unattended(case, inp):
     idx = mask.nonzero().view(-1).to(kc.device)
     if idx.numel():
         for c in (kc, vc):
-            c.view(n_slots, *c.shape[2:]).index_fill_(0, idx, float("nan"))
+            if c.dtype == torch.float8_e4m3fn:  # E4M3 NaN code S.1111.111
+                c.view(torch.uint8).view(n_slots, *c.shape[2:]).index_fill_(0, idx, 0x7F)
+            else:
+                c.view(n_slots, *c.shape[2:]).index_fill_(0, idx, float("nan"))
     return int(idx.numel())
 
 
@@ -55,6 +58,8 @@ def run(case, dinp, layout="token_major", split_len=0, q=None, handle=None):
     h = handle or kb.KVAttn.for_case(case, layout=layout)
     if split_len:
         h.set_split_len(split_len)
+    if getattr(case, "kv_dtype", None) == "fp8":
+        h.set_kv_scales(dinp["k_scale"], dinp["v_scale"])
     kc, vc = dinp["k_cache"], dinp["v_cache"]
     if layout == "head_major":
         kc, vc = to_head_major(case, kc), to_head_major(case, vc)

@@ -1,7 +1,7 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration the
-benchmark times (automatic split plan, token-major caches): sampled output rows
-against the oracle computed row by row, plus NaN poison in never-attended slots
-and the sharp (q x 8) variant of each."""
+"""GPU parity at the workloads' full sizes (the five, and the 8-bit-cache versions of
+three of them), in the launch configuration the benchmark times (automatic plan,
+head-major caches): sampled output rows against the oracle computed row by row, plus
+NaN poison in never-attended slots and the sharp (q x 8) variant of each."""
 import numpy as np
 import pytest
 import torch
@@ -36,11 +36,12 @@ def test_full_size_sampled_rows(name, q_scale):
     host_meta = {"block_table": d["block_table"].cpu() if d["block_table"] is not None else None,
                  "seq_lens": d["seq_lens"].cpu(), "k_cache": d["k_cache"], "v_cache": d["v_cache"]}
     n_poison = gh.poison_unattended(case, host_meta)
-    h = kb.KVAttn.for_case(case)
-    out = gh.run(case, d, handle=h)
+    h = kb.KVAttn.for_case(case, layout="head_major")
+    out = gh.run(case, d, layout="head_major", handle=h)
     rows = _sample_rows(case)
     ref = oracle.decode_rows(case, d["q"], d["k_cache"], d["v_cache"], host_meta["block_table"],
-                             host_meta["seq_lens"], rows)
+                             host_meta["seq_lens"], rows, k_scale=d["k_scale"],
+                             v_scale=d["v_scale"])
     got = out.float().cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
     max_abs, rel = gh.check(got, ref, case.dtype, name)
     print(f"{name}: rows={len(rows)} poisoned={n_poison} max_abs={max_abs:.3g} rel={rel:.3g} "
