@@ -23,6 +23,13 @@ FLAGS = [
     "-fvisibility=hidden", "-Wall",
     # no packed fp32 arithmetic on the device (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leave branches on wave-uniform conditions unstructured: the decode tile loops
+    # branch only on scalars, and structuring them added paths on which the
+    # compiler's load-wait counts fell to zero at the loop head
+    "-mllvm", "-structurizecfg-skip-uniform-regions=true",
+    # keep all-lane LDS atomics as written (the atomic optimizer turns them into a
+    # single-lane atomic behind a lane-divergent branch, which brings structuring back)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
 

@@ -40,20 +40,28 @@ namespace kvattn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Lane geometry for a cache of element type KT: one 16-byte load per lane covers
-// EPL consecutive elements of a (position, head) row.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Per-lane load of a cache of element type KT: 16 bytes, or 8 for 8-bit codes (8
+// elements a lane either way, which keeps the lane's accumulators and query
+// fragment the size of the 16-bit case).
+template <int KT> struct KVec { typedef u32x4 T; static constexpr int DW = 4; };
+template <> struct KVec<FP8> { typedef u32x2 T; static constexpr int DW = 2; };
+
+// Lane geometry for a cache of element type KT: one load per lane covers EPL
+// consecutive elements of a (position, head) row.
 template <int KT, int D>
 struct Geo {
     static constexpr int EB = Elem<KT>::bytes;
-    static constexpr int EPL = 16 / EB;   // elements per lane (one 16-byte load)
-    static constexpr int LPR = D / EPL;   // lanes per (position, head) row
+    static constexpr int EPL = KVec<KT>::DW * 4 / EB;  // elements per lane (one load)
+    static constexpr int LPR = D / EPL;                // lanes per (position, head) row
 };
 
-// A lane's query elements (EPL of them, type DT): one 16-byte load, or two when
-// the cache holds 8-bit codes and the query 16-bit values.
+// A lane's query elements (EPL of them, type DT): one 16-byte load.
 template <int DT, int KT>
 struct QFrag {
-    static constexpr int N = (16 / Elem<KT>::bytes) * Elem<DT>::bytes / 16;
+    static constexpr int N = (KVec<KT>::DW * 4 / Elem<KT>::bytes) * Elem<DT>::bytes / 16;
+    static_assert(N == 1, "one 16-byte query load per lane");
     u32x4 w[N];
 };
 
@@ -95,15 +103,15 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // value) and fed to the same packed dot products.  The K scale is applied to the
 // score by the caller.
 template <int DT, int KT>
-__device__ __forceinline__ float dot_q(const QFrag<DT, KT>& q, const u32x4& k) {
+__device__ __forceinline__ float dot_q(const QFrag<DT, KT>& q, const typename KVec<KT>::T& k) {
     if constexpr (KT != FP8) {
         return dot16<DT>(q.w[0], k);
     } else {
         float s = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 2; ++e) {
             const uint32_t w = k[e];  // codes of elements 4e .. 4e+3
-            const uint32_t q0 = q.w[e / 2][(2 * e) % 4], q1 = q.w[e / 2][(2 * e) % 4 + 1];
+            const uint32_t q0 = q.w[0][2 * e], q1 = q.w[0][2 * e + 1];
             if constexpr (DT == F16) {
                 const half2_t k0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
                 const half2_t k1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
@@ -122,11 +130,11 @@ __device__ __forceinline__ float dot_q(const QFrag<DT, KT>& q, const u32x4& k) {
     }
 }
 
-// one lane's 16 bytes of V as EPL floats (8-bit codes unscaled)
+// one lane's load of V as EPL floats (8-bit codes unscaled)
 template <int KT>
-__device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
+__device__ __forceinline__ void unpack16(const typename KVec<KT>::T& w, float* f) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < KVec<KT>::DW; ++e) {
         if constexpr (KT == F16) {
             f[2 * e] = f16_lo(w[e]);
             f[2 * e + 1] = f16_hi(w[e]);
@@ -143,6 +151,72 @@ __device__ __forceinline__ void unpack16(const u32x4& w, float* f) {
             f[4 * e + 3] = hi[1];
         } else {
             f[e] = __uint_as_float(w[e]);
+        }
+    }
+}
+
+// two fp32 -> one dword of two 16-bit values of type DT (round to nearest even)
+template <int DT>
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    if constexpr (DT == F16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// acc[r][e] += sum_u p[r][u] * v[u][e] for 8-bit V codes (unscaled), two positions
+// per packed dot product: a byte permute interleaves the codes of positions u and
+// u+1, one exact conversion gives the (v[u][e], v[u+1][e]) pair in the query's
+// 16-bit type, and v_dot2 adds p[r][u] v[u][e] + p[r][u+1] v[u+1][e] with the
+// weights rounded to that type (as the matrix-core path rounds P).  Paged caches:
+// codes behind an out-of-pool page entry are replaced by 0 (= +0.0).
+template <int DT, int ROWS, int U, bool ZERO_BAD>
+__device__ __forceinline__ void accumulate_fp8_pairs(const u32x2 (&vw)[U], const bool (&vok)[U],
+                                                     const float (&pw)[ROWS][U],
+                                                     float (&acc)[ROWS][8]) {
+    static_assert(U % 2 == 0, "positions are taken in pairs");
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+        uint32_t pp[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) pp[r] = pack_pair<DT>(pw[r][u], pw[r][u + 1]);
+#pragma unroll
+        for (int e4 = 0; e4 < 2; ++e4) {
+            uint32_t w0 = vw[u][e4], w1 = vw[u + 1][e4];  // codes of elements 4e4 .. 4e4+3
+            if constexpr (ZERO_BAD) {
+                w0 = vok[u] ? w0 : 0u;
+                w1 = vok[u + 1] ? w1 : 0u;
+            }
+            // bytes (w0.0, w1.0, w0.1, w1.1) and (w0.2, w1.2, w0.3, w1.3)
+            const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+            const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+            // element 4e4 + k: pair k of (lo.low, lo.high, hi.low, hi.high)
+            if constexpr (DT == F16) {
+                const half2_t v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false),
+                                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true),
+                                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false),
+                                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true)};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int r = 0; r < ROWS; ++r)
+                        acc[r][4 * e4 + k] = __builtin_amdgcn_fdot2(
+                            __builtin_bit_cast(half2_t, pp[r]), v[k], acc[r][4 * e4 + k], false);
+            } else {
+                const bf16x2_t v[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false),
+                                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true),
+                                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false),
+                                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int r = 0; r < ROWS; ++r)
+                        acc[r][4 * e4 + k] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(short2_t, pp[r]), __builtin_bit_cast(short2_t, v[k]),
+                            acc[r][4 * e4 + k], false);
+            }
         }
     }
 }
@@ -165,7 +239,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
     const FlatPlan fp = plan_flat<THREADS>(p, n_wg);
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, so tile loops branch on scalars
     const int lw = tid % 64;
     const int lane = lw % LPR;
     const int lgw = lw / LPR;  // lane group within the wave
@@ -231,11 +305,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
     bool val[U];
     const char* ka[U];
     int32_t blk[U];  // paged: page-table entries of the tile to address next
-    auto fetch_pages = [&](const Ctx& x, int32_t t) __attribute__((always_inline)) {
+    auto fetch_pages = [&](const Ctx& x, int32_t t, int32_t (&dst)[U]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int32_t j = min(x.ja + t * TWW + u * LGW + lgw, x.jb - 1);
-            blk[u] = page_entry(p, x.b, span_pos(x.s, j));
+            dst[u] = page_entry(p, x.b, span_pos(x.s, j));
         }
     };
     auto address = [&](const Ctx& x, int32_t t) __attribute__((always_inline)) {
@@ -256,17 +330,22 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             }
         }
     };
-    u32x4 kw[U], vw[U];
-    // Issue the loads of wave tile t of a piece (its Q rows too when `with_q`).
+    using KVT = typename KVec<KT>::T;
+    // K and V words of the tile being computed and of the next one, in two buffers
+    // whose roles alternate (the tile loop is unrolled by two), so that the next
+    // tile's loads land in registers of their own and stay in flight across the
+    // current tile's arithmetic: no register copies, no wait at the loop's end.
+    KVT kwA[U], vwA[U], kwB[U], vwB[U];
+    // Issue the loads of the wave's first tile of a piece (and the piece's Q rows).
     auto first_loads = [&](const Ctx& x, QF (&qv)[ROWS]) __attribute__((always_inline)) {
         load_q(x, qv);
         if (wave < x.n_tiles) {
-            if constexpr (CACHE == PAGED) fetch_pages(x, wave);
+            if constexpr (CACHE == PAGED) fetch_pages(x, wave, blk);
             address(x, wave);
 #pragma unroll
-            for (int u = 0; u < U; ++u) kw[u] = *reinterpret_cast<const u32x4*>(ka[u]);
+            for (int u = 0; u < U; ++u) kwA[u] = *reinterpret_cast<const KVT*>(ka[u]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) vw[u] = *reinterpret_cast<const u32x4*>(ka[u] + dv);
+            for (int u = 0; u < U; ++u) vwA[u] = *reinterpret_cast<const KVT*>(ka[u] + dv);
         }
     };
 
@@ -313,21 +392,27 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
         }
 
         int32_t cur = wave;
-        // next tile for this wave: one LDS atomic per tile, issued a tile ahead
-        // (deterministic mode: every NWAVES-th tile, a fixed summation order)
-        auto grab = [&]() __attribute__((always_inline)) -> int32_t {
-            if (p.deterministic) return cur + NWAVES;
-            int32_t t = 0;
-            if (lw == 0)
-                t = __hip_atomic_fetch_add(&s_next_tile, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+        // the next tile for this wave (after tile `after`): one LDS atomic per tile,
+        // requested a tile ahead (two for paged caches, whose page-table entries are
+        // read as soon as the tile is granted); deterministic mode: every NWAVES-th tile,
+        // a fixed summation order.  Every lane takes part in the atomic (lane 0 adds
+        // 1, the others 0), so the loop holds no lane-divergent branch; lane 0's
+        // result is the tile granted.
+        auto grab = [&](int32_t after) __attribute__((always_inline)) -> int32_t {
+            if (p.deterministic) return after + NWAVES;
+            const int32_t t = __hip_atomic_fetch_add(&s_next_tile, lw == 0 ? 1 : 0,
+                                                     __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
             return __builtin_amdgcn_readfirstlane(t);
         };
-        int32_t nxt = cur < n_tiles ? grab() : n_tiles;
-        if constexpr (CACHE == PAGED) {
-            if (nxt < n_tiles) fetch_pages(x, nxt);
-        }
-        while (cur < n_tiles) {
+        int32_t nxt = cur < n_tiles ? grab(cur) : n_tiles;
+        if constexpr (CACHE == PAGED)
+            if (nxt < n_tiles) fetch_pages(x, nxt, blk);
+        // One tile: scores from kc; the next tile's loads into kn/vn (paged: first the
+        // page-table entries of the tile after it, so that every wait in the loop is
+        // for the oldest loads in flight); softmax update; P.V from vc.
+        auto tile = [&](const KVT (&kc)[U], const KVT (&vc)[U], KVT (&kn)[U], KVT (&vn)[U])
+                        __attribute__((always_inline)) {
             const bool more = nxt < n_tiles;
             // raw scores q.k; the softmax scale (times log2 e) is applied inside the
             // exp2 argument, so the running max m is kept in scaled units
@@ -336,7 +421,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             for (int r = 0; r < ROWS; ++r) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const float x = group_sum<LPR>(dot_q<DT, KT>(qv[r], kw[u]));
+                    const float x = group_sum<LPR>(dot_q<DT, KT>(qv[r], kc[u]));
                     bool ok = val[u];
                     if constexpr (MASKED)
                         ok = ok & (pos[u] <= hi[r]) & ((pos[u] < p.n_sink) | (pos[u] >= lo[r]));
@@ -348,11 +433,19 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             bool vok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) vok[u] = val[u];
-            if (more) {
-                address(x, nxt);
-#pragma unroll
-                for (int u = 0; u < U; ++u) kw[u] = *reinterpret_cast<const u32x4*>(ka[u]);
+            // The next tile's loads are issued unconditionally (past the last tile they
+            // re-read this tile's valid addresses), which keeps the loop free of
+            // merges of loaded and not-loaded registers.
+            if (more) address(x, nxt);
+            int32_t n2 = n_tiles;
+            if constexpr (CACHE == PAGED) {
+                if (more) n2 = grab(nxt);
+                if (n2 < n_tiles) fetch_pages(x, n2, blk);
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u) kn[u] = *reinterpret_cast<const KVT*>(ka[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) vn[u] = *reinterpret_cast<const KVT*>(ka[u] + dv);
             float pw[ROWS][U];
 #pragma unroll
             for (int r = 0; r < ROWS; ++r) {
@@ -374,10 +467,13 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
                 }
                 m[r] = m_new;
             }
+            if constexpr (KT == FP8) {
+                accumulate_fp8_pairs<DT, ROWS, U, CACHE == PAGED>(vc, vok, pw, acc);
+            } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float vf[EPL];
-                unpack16<KT>(vw[u], vf);
+                unpack16<KT>(vc[u], vf);
                 if constexpr (CACHE == PAGED) {
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) vf[e] = vok[u] ? vf[e] : 0.0f;
@@ -387,17 +483,25 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(pw[r][u], vf[e], acc[r][e]);
             }
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) vw[u] = *reinterpret_cast<const u32x4*>(ka[u] + dv);
             }
             cur = nxt;
-            if (cur < n_tiles) {
-                nxt = grab();
-                if constexpr (CACHE == PAGED) {
-                    if (nxt < n_tiles) fetch_pages(x, nxt);
-                }
+            if constexpr (CACHE == PAGED) {
+                nxt = n2;
+            } else {
+                if (cur < n_tiles) nxt = grab(cur);
             }
+        };
+        // Enter the tile loop with no vector memory operation in flight (the first
+        // tile's loads, the previous piece's stores and the first page-table entries
+        // complete here).  The compiler's wait counts in the loop hold on every path
+        // into it, so they only need to cover the oldest loads in flight; with other
+        // operations pending on entry they fall to zero and each tile would wait for
+        // the next tile's loads.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unconstrained
+        while (cur < n_tiles) {
+            tile(kwA, vwA, kwB, vwB);
+            if (cur >= n_tiles) break;
+            tile(kwB, vwB, kwA, vwA);
         }
 
         if (has_next) {
@@ -485,6 +589,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
 #ifndef KVATTN_VALU_U_MID
 #define KVATTN_VALU_U_MID 4     // 4 rows
 #endif
+#ifndef KVATTN_VALU_U8_FACTOR
+#define KVATTN_VALU_U8_FACTOR 1
+#endif
 #ifndef KVATTN_VALU_U_LARGE
 #define KVATTN_VALU_U_LARGE 4   // 8 or 16 rows
 #endif
@@ -502,8 +609,11 @@ constexpr int valu_waves(int rows_per_block) {
 
 template <int DT, int KT, int D, int ROWS, int CACHE>
 inline const void* valu_kernel_t(bool masked) {
-    constexpr int U = ROWS <= 2 ? KVATTN_VALU_U_SMALL
-                                : (ROWS <= 4 ? KVATTN_VALU_U_MID : KVATTN_VALU_U_LARGE);
+    // 8-bit caches with 1-2 rows: KVATTN_VALU_U8_FACTOR times the positions per
+    // tile, so a tile moves as many bytes as a 16-bit one
+    constexpr int U = (KT == FP8 && ROWS <= 2 ? KVATTN_VALU_U8_FACTOR : 1) *
+                      (ROWS <= 2 ? KVATTN_VALU_U_SMALL
+                                 : (ROWS <= 4 ? KVATTN_VALU_U_MID : KVATTN_VALU_U_LARGE));
     constexpr int NW = valu_waves(ROWS);
     return masked
                ? reinterpret_cast<const void*>(&decode_valu_kernel<DT, KT, D, ROWS, CACHE, U, true, NW>)
