@@ -131,7 +131,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     const FlatPlan fp = plan_flat<MFMA_THREADS>(p, n_wg);
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform: scalar branches
     const int l = tid % 64;
     const int lr = l % 16;  // operand row / output column
     const int lq = l / 16;  // operand k-group / output row group
@@ -224,16 +224,20 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     // iteration, so the LDS atomic's latency is not waited for.
     const int32_t n_tiles = (j1 - j0 + TILE - 1) / TILE;
     if (tid == 0) s_next_tile = MFMA_WAVES;
+    // Every lane takes part in the atomic (lane 0 adds 1, the others 0): no
+    // lane-divergent branch in the tile loop.
     auto grab = [&](int32_t after) __attribute__((always_inline)) -> int32_t {
         if (p.deterministic) return after + MFMA_WAVES;
-        int32_t t = 0;
-        if (l == 0)
-            t = __hip_atomic_fetch_add(&s_next_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int32_t t = __hip_atomic_fetch_add(&s_next_tile, l == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         return __builtin_amdgcn_readfirstlane(t);
     };
 
     // One register buffer each for K and V: the next tile's V is loaded as soon as
-    // this tile's V sits in LDS, the next K as soon as S^T has consumed this K.
+    // this tile's V sits in LDS, the next K as soon as S^T has consumed this K.  The
+    // loads are issued unconditionally (past the last tile, positions clamp to the
+    // piece's last one), so no path through the loop lacks them and the compiler's
+    // waits stay partial: V staging waits for V only, S^T for K only.
     u32x4 kc[2][KS], vr[NV];
     int32_t cur = wave;
     if (cur < n_tiles) {
@@ -260,6 +264,9 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     }
     const float c = p.scale_log2;
 
+    // enter the loop with no vector memory operation pending, so its head sees the
+    // same state from every path
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unconstrained
     while (cur < n_tiles) {
         const int32_t tb = j0 + cur * TILE;
         const bool more = nxt < n_tiles;
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             }
             *reinterpret_cast<u32x4*>(vbuf + (v * PPI + l / CPR) * VROW + (l % CPR) * 16) = x;
         }
-        if (more) load_v(j0 + nxt * TILE, vr);
+        load_v(j0 + nxt * TILE, vr);
 
         // S^T = K . Q^T
         f32x4 st[2][R];
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
                     acc = mfma16x16x32<DT>(kc[tt][ks], qsm[(qt * KS + ks) * 64 + l], acc);
                 st[tt][qt] = acc;
             }
-        if (more) load_k(j0 + nxt * TILE, kc);
+        load_k(j0 + nxt * TILE, kc);
 
         // Mask only where it can bite: a partial tile, rows that do not all see the
         // tile's last position (q_len > 1), the window mask, or (paged) a bad entry.
