@@ -142,6 +142,39 @@ KVATTN_API int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cach
                   const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,
                   int32_t mask_mode, int32_t n_sink, int32_t window, void* out);
 
+/*
+ * Enqueue the write of each sequence's q_len new K and V rows into the caches:
+ * row i of sequence b goes to the slot of logical position P = T_b - q_len + i
+ * (T_b = seq_lens[b]) - the step of a decode that writes the new token's key and
+ * value back to memory before attending (dothoosh.com speculative-decoding
+ * article, "bypassing the memory bottleneck"), through the same position-to-slot
+ * mapping the decode reads with: CONTIGUOUS slot P; PAGED block
+ * block_table[b][P / block_size], offset P % block_size (lesson, "PagedAttention");
+ * RING the first n_sink positions keep their slots, later ones roll over the other
+ * capacity - n_sink slots, overwriting the position capacity - n_sink earlier
+ * (StreamingLLM article, "The StreamingLLM solution").
+ *   k_new, v_new [batch, q_len, Hkv, D], the caches' element type   device, read
+ *   k_cache, v_cache  caches (layout above)                          device, written
+ *   block_table, seq_lens                                            as for kvattn_decode
+ *   q_len        1 .. max_q_len
+ *   n_sink       RING: the sink count the decodes use (0 .. capacity - 1); else ignored
+ * Rows without a slot are not written: P < 0 (T < q_len), P >= capacity (CONTIGUOUS,
+ * PAGED), or a page-table entry outside [0, num_blocks).  Only the new rows' slots
+ * are written.  Pointers 16-byte aligned.  No allocation, no synchronisation.
+ */
+KVATTN_API int kvattn_append(kvattn_handle* h, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                             int32_t q_len, int32_t n_sink);
+
+/* kvattn_append followed by kvattn_decode on the same stream (two launches, in that
+ * order): the decode sees the rows just written.  Arguments as for the two calls;
+ * a RING cache uses n_sink for both (with KVATTN_MASK_SINK_WINDOW). */
+KVATTN_API int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int32_t q_len, int32_t mask_mode, int32_t n_sink,
+                                    int32_t window, void* out);
+
 /* Free the workspace and the handle.  NULL is a no-op.  No enqueued decode may
  * still be using the handle. */
 KVATTN_API void kvattn_destroy(kvattn_handle* h);

@@ -27,7 +27,8 @@ LAYOUT = {"token_major": 0, "head_major": 1}
 
 EXPORTS = ("kvattn_create", "kvattn_decode", "kvattn_destroy", "kvattn_set_stream",
            "kvattn_set_batch", "kvattn_set_split_len", "kvattn_set_kv_scales", "kvattn_plan",
-           "kvattn_workspace_bytes", "kvattn_last_error", "kvattn_debug_gather")
+           "kvattn_workspace_bytes", "kvattn_last_error", "kvattn_debug_gather", "kvattn_append",
+           "kvattn_append_decode")
 
 
 class kvattn_config(ctypes.Structure):
@@ -82,6 +83,10 @@ def load() -> ctypes.CDLL:
     lib.kvattn_last_error.restype = ctypes.c_char_p
     lib.kvattn_debug_gather.argtypes = [H, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.kvattn_debug_gather.restype = ctypes.c_int
+    lib.kvattn_append.argtypes = [H, vp, vp, vp, vp, vp, vp, i32, i32]
+    lib.kvattn_append.restype = ctypes.c_int
+    lib.kvattn_append_decode.argtypes = [H, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.kvattn_append_decode.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -126,6 +131,23 @@ def kvattn_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len: int, mas
                                 _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_table, "block_table"),
                                 _dev_ptr(seq_lens, "seq_lens"), q_len, mask_mode, n_sink, window,
                                 _dev_ptr(out, "out")), "kvattn_decode")
+
+
+def kvattn_append(h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len: int,
+                  n_sink: int) -> None:
+    _check(load().kvattn_append(h, _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+                                _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                _dev_ptr(block_table, "block_table"), _dev_ptr(seq_lens, "seq_lens"),
+                                q_len, n_sink), "kvattn_append")
+
+
+def kvattn_append_decode(h, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len: int,
+                         mask_mode: int, n_sink: int, window: int, out) -> None:
+    _check(load().kvattn_append_decode(
+        h, _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+        _dev_ptr(block_table, "block_table"), _dev_ptr(seq_lens, "seq_lens"), q_len, mask_mode,
+        n_sink, window, _dev_ptr(out, "out")), "kvattn_append_decode")
 
 
 def kvattn_destroy(h) -> None:
@@ -251,6 +273,32 @@ class KVAttn:
         kvattn_set_stream(self.h, st.cuda_stream)
         kvattn_decode(self.h, q, k_cache, v_cache, block_table, seq_lens, q_len, MASK[mask_mode],
                       n_sink, window, out)
+        return out
+
+    def _check_types(self, **tensors):
+        for name, t in tensors.items():
+            want = TORCH_DTYPE[self.dtype] if name == "q" else TORCH_DTYPE[self.kv_dtype]
+            if t.dtype != want:
+                raise ValueError(f"{name} must be {want}")
+
+    def append(self, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len: int,
+               n_sink: int = 0, stream: Optional[torch.cuda.Stream] = None) -> None:
+        """Writes the new rows k_new, v_new [batch, q_len, Hkv, D] into the caches."""
+        self._check_types(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache)
+        st = stream if stream is not None else torch.cuda.current_stream(k_new.device)
+        kvattn_set_stream(self.h, st.cuda_stream)
+        kvattn_append(self.h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len, n_sink)
+
+    def append_decode(self, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len: int,
+                      mask_mode: str = "causal", n_sink: int = 0, window: int = 0, out=None,
+                      stream: Optional[torch.cuda.Stream] = None):
+        self._check_types(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache)
+        if out is None:
+            out = torch.empty_like(q)
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        kvattn_set_stream(self.h, st.cuda_stream)
+        kvattn_append_decode(self.h, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                             q_len, MASK[mask_mode], n_sink, window, out)
         return out
 
     def debug_gather(self, block_table, seq_lens, q_len: int, mask_mode: str = "causal",

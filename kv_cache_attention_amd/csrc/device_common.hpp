@@ -36,6 +36,8 @@ struct DecodeParams {
     int32_t seg_rows;     // rows per segment as laid out in the workspace
     int32_t min_chunk;    // smallest unit (positions)
     int32_t units_per_wg; // units per workgroup the flat range is cut into
+    int32_t tail_pct;     // share (percent) of the flat range left to a dynamic tail (0: none)
+    int32_t tail_units;   // tail units per workgroup
     int32_t deterministic;  // waves take fixed tiles instead of a shared queue
     const float* k_scale; // 8-bit caches: [Hkv] dequantisation scales (else NULL)
     const float* v_scale;

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "append.hpp"
+
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -24,17 +26,28 @@ int fail(int code, const std::string& msg) {
 }
 
 // Work decomposition: the flat list of (sequence, KV head, row block) segments is
-// cut into equal units, about kUnitsPerWg per workgroup, with as many workgroups
-// as the GPU holds resident at once for the kernel instance (occupancy x compute
-// units); workgroups take units from a device-wide queue.  A unit is at least
-// kMinChunk positions (kMinChunkMfma for the matrix-core kernel, whose per-piece
-// epilogue is heavier).  The split points are placed on the device from seq_lens.
+// cut into kUnitsPerWg large units per workgroup, with as many workgroups as the
+// GPU holds resident at once for the kernel instance (occupancy x compute units),
+// and a tail of kTailPct percent of the work in about kTailUnits smaller units per
+// workgroup that a device-wide queue hands to whichever workgroup is free.  A unit
+// is at least kMinChunk positions (kMinChunkMfma for the matrix-core kernel, whose
+// per-piece epilogue is heavier).  The split points are placed on the device from
+// seq_lens.
 #ifndef KVATTN_UNITS_PER_WG
 #define KVATTN_UNITS_PER_WG 1
 #endif
+#ifndef KVATTN_TAIL_PCT
+#define KVATTN_TAIL_PCT 0
+#endif
+#ifndef KVATTN_TAIL_UNITS
+#define KVATTN_TAIL_UNITS 2
+#endif
 constexpr int kMaxResidentWorkgroups = 1024;
 constexpr int kMinForcedUnits = 512;
-constexpr int kUnitsPerWg = KVATTN_UNITS_PER_WG;  // units of the flat range per workgroup
+constexpr int kUnitsPerWg = KVATTN_UNITS_PER_WG;  // large units per workgroup
+constexpr int kTailPct = KVATTN_TAIL_PCT;         // share of the work in the tail
+constexpr int kTailUnits = KVATTN_TAIL_UNITS;     // tail units per workgroup
+static_assert(kTailPct >= 0 && kTailPct < 100 && kTailUnits >= 1, "tail shape");
 constexpr int kMinChunk = 256;
 constexpr int kMinChunkMfma = 512;
 constexpr int kChunkQuantum = 64;
@@ -206,16 +219,17 @@ int resident_workgroups(kvattn_handle* h, int q_len) {
 
 // Partial rows the workspace needs for decodes with q_len: one slot per unit plus
 // one per segment (the pieces of a step fill at most that many), each holding a
-// segment's rows.  Units: at most kUnitsPerWg per launched workgroup (at most
-// kMaxResidentWorkgroups), and no more than the longest possible flat range holds
-// at the default minimum unit; forced unit lengths (tests) may use up to
-// kMinForcedUnits.  Host-only: the bound does not depend on the device.
+// segment's rows.  Units: at most kUnitsPerWg + kTailUnits per launched workgroup
+// (at most kMaxResidentWorkgroups), and no more than one plus what the longest
+// possible flat range holds at the default minimum unit (every unit is at least
+// that long; the head/tail boundary adds one); forced unit lengths (tests) may use
+// up to kMinForcedUnits.  Host-only: the bound does not depend on the device.
 int64_t part_rows_for(const kvattn_config& c, int q_len) {
     const int64_t segs = (int64_t)c.max_batch * segs_per_seq_of(c, q_len);
     const int64_t w_max = segs * max_attended(c, q_len, KVATTN_MASK_CAUSAL, 0, 0);
     const int64_t by_len = ceil_div(w_max, use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk);
-    const int64_t units = std::min<int64_t>((int64_t)kMaxResidentWorkgroups * kUnitsPerWg,
-                                            std::max<int64_t>(by_len, kMinForcedUnits));
+    const int64_t units = std::min<int64_t>((int64_t)kMaxResidentWorkgroups * (kUnitsPerWg + kTailUnits),
+                                            std::max<int64_t>(by_len + 1, kMinForcedUnits));
     return (units + segs) * seg_rows_of(c, q_len);
 }
 
@@ -243,7 +257,9 @@ int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
                                      : (use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk);
     const int64_t units_max = ceil_div(w_max, *min_chunk);  // units are >= min_chunk
     const int64_t g = std::min<int64_t>(resident_workgroups(h, q_len), units_max);
-    const int64_t units = h->forced_chunk > 0 ? units_max : std::min<int64_t>(units_max, g * kUnitsPerWg);
+    const int64_t units = h->forced_chunk > 0
+                              ? units_max
+                              : std::min<int64_t>(units_max + 1, g * (kUnitsPerWg + kTailUnits));
     const int64_t need =
         (units + (int64_t)h->batch * segs_per_seq_of(c, q_len)) * seg_rows_of(c, q_len);
     if (need > h->ws_part_rows)
@@ -409,6 +425,8 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.seg_rows = seg_rows_of(c, q_len);
     p.min_chunk = min_chunk;
     p.units_per_wg = h->forced_chunk > 0 ? 1 << 30 : kUnitsPerWg;  // forced: units of exactly min_chunk
+    p.tail_pct = h->forced_chunk > 0 ? 0 : kTailPct;
+    p.tail_units = kTailUnits;
     p.deterministic = (c.flags & KVATTN_FLAG_DETERMINISTIC) ? 1 : 0;
     p.k_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->k_scale : nullptr;
     p.v_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->v_scale : nullptr;
@@ -416,9 +434,16 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.scale_log2 = scale * 1.4426950408889634f;
 }
 
-int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const void* v_cache,
-                  const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,
-                  int32_t mask_mode, int32_t n_sink, int32_t window, void* out) {
+}  // extern "C"
+
+namespace {
+
+// Checks and parameters of a decode; *grid = 0 when there is nothing to launch.
+int prepare_decode(kvattn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,
+                   int32_t mask_mode, int32_t n_sink, int32_t window, void* out,
+                   kvattn::DecodeParams& p, int* grid) {
+    *grid = 0;
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
     int rc = validate_decode_args(h, q_len, mask_mode, n_sink, window);
     if (rc) return rc;
@@ -431,12 +456,16 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
         return fail(KVATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
     if (kv_dtype_of(h->cfg) == KVATTN_FP8_E4M3 && (!h->k_scale || !h->v_scale))
         return fail(KVATTN_ERR_INVALID_ARG, "an 8-bit cache needs kvattn_set_kv_scales first");
-    int grid, chunk;
-    rc = plan_for(h, q_len, mask_mode, n_sink, window, &grid, &chunk);
+    int chunk;
+    rc = plan_for(h, q_len, mask_mode, n_sink, window, grid, &chunk);
     if (rc) return rc;
-    kvattn::DecodeParams p;
     fill_params(h, p, q, k_cache, v_cache, block_table, seq_lens, q_len, mask_mode, n_sink,
                 window, out, chunk);
+    return KVATTN_OK;
+}
+
+int launch_decode(kvattn_handle* h, const kvattn::DecodeParams& p, int grid, int32_t q_len) {
+    if (grid == 0) return KVATTN_OK;
     hipError_t e =
         use_mfma(h->cfg, q_len)
             ? kvattn::launch_decode_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
@@ -445,6 +474,103 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
     if (e != hipSuccess)
         return fail(KVATTN_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return KVATTN_OK;
+}
+
+// Checks and parameters of an append; a->n_chunks = 0 when there is nothing to write.
+int prepare_append(kvattn_handle* h, const void* k_new, const void* v_new, void* k_cache,
+                   void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                   int32_t q_len, int32_t n_sink, kvattn::AppendParams* a) {
+    a->n_chunks = 0;
+    if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
+    const kvattn_config& c = h->cfg;
+    if (q_len < 1) return fail(KVATTN_ERR_INVALID_ARG, "q_len must be >= 1");
+    if (q_len > c.max_q_len) return fail(KVATTN_ERR_CAPACITY, "q_len exceeds max_q_len");
+    if (c.cache_mode == KVATTN_RING && (n_sink < 0 || (int64_t)n_sink + q_len > c.capacity))
+        return fail(KVATTN_ERR_INVALID_ARG, "ring append: need 0 <= n_sink and n_sink + q_len <= capacity");
+    if (h->batch == 0) return KVATTN_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens)
+        return fail(KVATTN_ERR_INVALID_ARG, "k_new, v_new, caches and seq_lens must be non-NULL");
+    if ((c.cache_mode == KVATTN_PAGED) != (block_table != nullptr))
+        return fail(KVATTN_ERR_INVALID_ARG, "block_table must be given exactly for a paged cache");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(KVATTN_ERR_INVALID_ARG, "k_new, v_new and caches must be 16-byte aligned");
+    const int kv = kv_dtype_of(c);
+    const int eb = kv == KVATTN_F32 ? 4 : (kv == KVATTN_FP8_E4M3 ? 1 : 2);
+    a->k_new = static_cast<const char*>(k_new);
+    a->v_new = static_cast<const char*>(v_new);
+    a->k_cache = static_cast<char*>(k_cache);
+    a->v_cache = static_cast<char*>(v_cache);
+    a->block_table = block_table;
+    a->seq_lens = seq_lens;
+    a->stride_seq = h->stride_seq;
+    a->stride_head = h->stride_head;
+    a->stride_tok = h->stride_tok;
+    a->batch = h->batch;
+    a->num_kv_heads = c.num_kv_heads;
+    a->q_len = q_len;
+    a->elem_bytes = eb;
+    a->row_bytes = c.head_dim * eb;  // a multiple of 16 (head_dim 64 or 128)
+    a->cache_mode = c.cache_mode;
+    a->capacity = c.capacity;
+    a->log2_block = c.cache_mode == KVATTN_PAGED ? ilog2(c.block_size) : 0;
+    a->num_blocks = c.cache_mode == KVATTN_PAGED ? c.num_blocks : 0;
+    a->blocks_per_seq = c.cache_mode == KVATTN_PAGED ? c.capacity / c.block_size : 0;
+    a->n_sink = c.cache_mode == KVATTN_RING ? n_sink : 0;
+    a->n_chunks = 2 * (int64_t)h->batch * q_len * c.num_kv_heads * (a->row_bytes / 16);
+    return KVATTN_OK;
+}
+
+int launch_append(kvattn_handle* h, const kvattn::AppendParams& a) {
+    hipError_t e = kvattn::launch_append(a, h->stream);
+    if (e != hipSuccess)
+        return fail(KVATTN_ERR_HIP, std::string("append launch: ") + hipGetErrorString(e));
+    return KVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,
+                  int32_t mask_mode, int32_t n_sink, int32_t window, void* out) {
+    kvattn::DecodeParams p;
+    int grid;
+    int rc = prepare_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len, mask_mode,
+                            n_sink, window, out, p, &grid);
+    if (rc) return rc;
+    return launch_decode(h, p, grid, q_len);
+}
+
+int kvattn_append(kvattn_handle* h, const void* k_new, const void* v_new, void* k_cache,
+                  void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                  int32_t q_len, int32_t n_sink) {
+    kvattn::AppendParams a;
+    int rc = prepare_append(h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len,
+                            n_sink, &a);
+    if (rc) return rc;
+    return a.n_chunks > 0 ? launch_append(h, a) : KVATTN_OK;
+}
+
+int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t q_len, int32_t mask_mode,
+                         int32_t n_sink, int32_t window, void* out) {
+    // every check of both calls first, so an error launches nothing
+    kvattn::DecodeParams p;
+    int grid;
+    int rc = prepare_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len, mask_mode,
+                            n_sink, window, out, p, &grid);
+    if (rc) return rc;
+    kvattn::AppendParams a;
+    rc = prepare_append(h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len,
+                        mask_mode == KVATTN_MASK_SINK_WINDOW ? n_sink : 0, &a);
+    if (rc) return rc;
+    if (a.n_chunks > 0) {
+        rc = launch_append(h, a);
+        if (rc) return rc;
+    }
+    return launch_decode(h, p, grid, q_len);
 }
 
 int kvattn_debug_gather(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,

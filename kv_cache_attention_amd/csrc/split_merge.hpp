@@ -99,21 +99,15 @@ struct MergeSmem {
     float4 red[THREADS];
 };
 
-// Called by every thread of the workgroup after it wrote its partial of rows
-// row0 .. row0 + NROWS - 1 of KV head kvh into slot slot0 + (its piece).  Returns
-// after the merge (last workgroup of the segment) or right away (the others).
+// Merges the nvalid partials of rows row0 .. row0 + NROWS - 1 of KV head kvh
+// (slots slot0 ..) into the output and puts the segment's counter back to zero.
+// Called by every thread of the workgroup that drew the segment's last ticket.
 template <int DT, int D, int NROWS, int THREADS>
-__device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0, int64_t unit,
-                                 int64_t slot0, int nvalid, MergeSmem<NROWS, THREADS>& sm) {
+__device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int kvh, int row0,
+                                               int64_t unit, int64_t slot0, int nvalid,
+                                               MergeSmem<NROWS, THREADS>& sm) {
     static_assert(THREADS % 64 == 0, "whole waves");
-    __shared__ int s_last;
     const int tid = threadIdx.x;
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
-    __syncthreads();                 // ... and every other thread's
-    if (tid == 0) s_last = atomicAdd(p.counters + unit, 1) == nvalid - 1;
-    __syncthreads();
-    if (!s_last) return;
-
     constexpr float NEG_INF = -__builtin_inff();
     const int NR = p.seg_rows;  // partial k of row r: index (slot0 + k) * NR + r
     const PartialReader rd(p);
@@ -239,6 +233,20 @@ __device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, int b, i
         }
     }
     if (tid == 0) atomicExch(p.counters + unit, 0);  // ready for the next call
+}
+
+// Called by every thread of the workgroup after it wrote its partial of rows
+// row0 .. row0 + NROWS - 1 of KV head kvh into slot slot0 + (its piece).  Returns
+// after the merge (last workgroup of the segment) or right away (the others).
+template <int DT, int D, int NROWS, int THREADS>
+__device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0, int64_t unit,
+                                 int64_t slot0, int nvalid, MergeSmem<NROWS, THREADS>& sm) {
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
+    __syncthreads();                 // ... and every other thread's
+    if (threadIdx.x == 0) s_last = atomicAdd(p.counters + unit, 1) == nvalid - 1;
+    __syncthreads();
+    if (s_last) merge_partials<DT, D, NROWS, THREADS>(p, b, kvh, row0, unit, slot0, nvalid, sm);
 }
 
 }  // namespace kvattn

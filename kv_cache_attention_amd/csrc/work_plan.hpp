@@ -4,11 +4,14 @@
 // block of query rows), each holding the count_b positions sequence b attends
 // (all KV heads and row blocks of a sequence have the same count).  Laid end to
 // end in (b, KV head, row block) order they form one flat range of
-// W = sum_b count_b * segs_per_seq position-units, cut into n_units equal units
-// of usz positions, about units_per_wg per workgroup of a grid sized by the host
-// to what the GPU holds at once.  Workgroups take units from a device-wide queue,
-// so the step ends when the memory system has streamed everything, not when the
-// most poorly served compute unit has finished a fixed share.
+// W = sum_b count_b * segs_per_seq position-units, cut into units for a grid
+// sized by the host to what the GPU holds at once.  The head of the range is cut
+// into one large unit per workgroup (units_per_wg of them), which each workgroup
+// takes first; the last tail_pct percent into about tail_units smaller units per
+// workgroup, handed out by a device-wide queue to whichever workgroup is free.
+// Compute units are served by the memory system at rates that differ by 10-20 %
+// (from one die to the next, and within a die), so equal static shares end when
+// the slowest finishes; with the tail, the ones served faster take more of it.
 //
 // A unit crosses segment boundaries: its pieces are processed one after the
 // other.  A piece that is a whole segment writes the final rows; otherwise it
@@ -31,11 +34,23 @@ namespace kvattn {
 // sequences [b0, b0 + per) and their flat offsets [excl, excl + mine).
 struct FlatPlan {
     int64_t total;   // W
-    int64_t usz;     // positions per unit (the slices workgroups take)
+    int64_t big;     // positions per head unit
+    int64_t n_big;   // head units: [u * big, (u + 1) * big) for u < n_big
+    int64_t xb;      // n_big * big: where the tail starts (>= total: no tail)
+    int64_t small;   // positions per tail unit
     int64_t n_units;
     int b0, per;
     int64_t excl, mine;
 };
+
+// First flat index of unit u, and the unit holding flat index x (< total): the
+// units partition the range in order, so both are monotone.
+__device__ __forceinline__ int64_t unit_begin(const FlatPlan& f, int64_t u) {
+    return u < f.n_big ? u * f.big : f.xb + (u - f.n_big) * f.small;
+}
+__device__ __forceinline__ int64_t unit_of(const FlatPlan& f, int64_t x) {
+    return x < f.xb ? x / f.big : f.n_big + (x - f.xb) / f.small;
+}
 
 // Flat work of sequence b: attended positions x segments per sequence.
 __device__ __forceinline__ int64_t seq_work(const DecodeParams& p, int b) {
@@ -77,8 +92,29 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     const int64_t units = (int64_t)n_wg * p.units_per_wg;
     int64_t usz = (total + units - 1) / units;
     if (usz < p.min_chunk) usz = p.min_chunk;
-    f.usz = (usz + 15) & ~(int64_t)15;
-    f.n_units = (total + f.usz - 1) / f.usz;
+    usz = (usz + 15) & ~(int64_t)15;
+    // uniform units of usz positions, unless the tail applies: every workgroup has
+    // a head unit, and those (>= min_chunk) leave a tail to share
+    f.big = usz;
+    f.n_big = (total + usz - 1) / usz;
+    f.xb = f.n_big * usz;
+    f.small = usz;
+    if (p.tail_pct > 0 && f.n_big >= units) {
+        int64_t big = (usz * (100 - p.tail_pct) / 100) & ~(int64_t)15;
+        if (big < p.min_chunk) big = (p.min_chunk + 15) & ~(int64_t)15;
+        if (units * big < total) {
+            const int64_t rest = total - units * big;
+            const int64_t tu = (int64_t)n_wg * p.tail_units;
+            int64_t small = (rest + tu - 1) / tu;
+            if (small < p.min_chunk) small = p.min_chunk;
+            f.big = big;
+            f.n_big = units;
+            f.xb = units * big;
+            f.small = (small + 15) & ~(int64_t)15;
+        }
+    }
+    f.n_units = f.xb >= total ? (total + f.big - 1) / f.big
+                              : f.n_big + (total - f.xb + f.small - 1) / f.small;
     return f;
 }
 
@@ -127,8 +163,8 @@ struct Piece {
 template <typename F>
 __device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, const FlatPlan& fp,
                                                      int64_t u, F&& f) {
-    const int64_t x0 = u * fp.usz;
-    const int64_t x1 = min(x0 + fp.usz, fp.total);
+    const int64_t x0 = unit_begin(fp, u);
+    const int64_t x1 = min(unit_begin(fp, u + 1), fp.total);
     const SeqAt at = seq_at(p, fp, x0);
     int b = at.b;
     int64_t off_b = at.off;
@@ -146,8 +182,8 @@ __device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, cons
         const int64_t seg0 = off_b + (int64_t)pc.seg * sb.count;
         pc.ja = (int32_t)(x - seg0);
         pc.jb = (int32_t)min<int64_t>(sb.count, x1 - seg0);
-        const int64_t first = seg0 / fp.usz;
-        const int64_t last = (seg0 + sb.count - 1) / fp.usz;
+        const int64_t first = unit_of(fp, seg0);
+        const int64_t last = unit_of(fp, seg0 + sb.count - 1);
         pc.unit = (int64_t)b * p.segs_per_seq + pc.seg;
         pc.slot0 = first + pc.unit;
         pc.nparts = (int)(last - first + 1);

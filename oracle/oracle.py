@@ -286,3 +286,41 @@ def split_merge_np(q: np.ndarray, K: np.ndarray, V: np.ndarray, n_split: int,
     L = sum(l * math.exp(m - M) for m, l, _ in parts if l > 0)
     acc = sum(a * math.exp(m - M) for m, l, a in parts if l > 0)
     return acc / L
+
+
+def append_np(pr, k_cache, v_cache, k_new, v_new, block_table, seq_lens, n_sink: int = 0,
+              num_blocks: Optional[int] = None):
+    """KV append: copies of the token-major caches with row i of sequence b of
+    k_new / v_new [batch, q_len, Hkv, D] written to the slot of position
+    P = T_b - q_len + i - the new token's key and value written back before it is
+    attended (dothoosh.com speculative-decoding article, "bypassing the memory
+    bottleneck"); slots as in slot_np (contiguous; 16-token pages through the page
+    table, nextadmin.net lesson "PagedAttention"; the StreamingLLM ring whose sinks
+    keep their slots, "The StreamingLLM solution").  Rows without a slot are not
+    written: P < 0, P >= capacity (contiguous, paged), or a page-table entry outside
+    [0, num_blocks).  Stored values are copied unchanged (any element type)."""
+    kc, vc = k_cache.clone(), v_cache.clone()
+    Hkv, D = pr.num_kv_heads, pr.head_dim
+    kf, vf = kc.view(-1, Hkv, D), vc.view(-1, Hkv, D)
+    sl = [int(x) for x in (seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens)]
+    bt = None
+    if pr.cache_mode == "paged":
+        bt = np.asarray(block_table.cpu() if isinstance(block_table, torch.Tensor)
+                        else block_table, dtype=np.int64)
+    for b in range(len(sl)):
+        T = max(sl[b], 0)
+        for i in range(pr.q_len):
+            P = T - pr.q_len + i
+            if P < 0:
+                continue
+            if pr.cache_mode != "ring" and P >= pr.capacity:
+                continue
+            if pr.cache_mode == "paged":
+                blk = int(bt[b, P // pr.block_size])
+                if num_blocks is not None and not 0 <= blk < num_blocks:
+                    continue
+            slot = int(slot_np(pr.cache_mode, b, np.array([P]), pr.capacity, pr.block_size, bt,
+                               n_sink)[0])
+            kf[slot] = k_new[b, i]
+            vf[slot] = v_new[b, i]
+    return kc, vc
