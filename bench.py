@@ -91,8 +91,9 @@ def cpu_baseline(case, d, out, n_rows, step_bytes):
     sl = d["seq_lens"].cpu()
     threads = oracle.threads()
     t0 = time.perf_counter()
+    tm = d["tree_mask"].cpu() if d.get("tree_mask") is not None else None
     ref = oracle.decode_rows(case, q, kc, vc, bt, sl, rows, k_scale=d["k_scale"],
-                             v_scale=d["v_scale"])
+                             v_scale=d["v_scale"], tree_mask=tm)
     dt = time.perf_counter() - t0
     # the sample's share of the step's algorithmic bytes, so the rate is in the metric's unit
     byts = step_bytes * len(rows) / total
@@ -146,8 +147,12 @@ def main():
     mask = kb.MASK[case.mask_mode]
 
     def step(c):
-        kb.kvattn_decode(h.h, d["q"], kcs[c], vcs[c], d["block_table"], d["seq_lens"],
-                         case.q_len, mask, case.n_sink, case.window, out)
+        if case.mask_mode == "tree":
+            kb.kvattn_decode_tree(h.h, d["q"], kcs[c], vcs[c], d["block_table"], d["seq_lens"],
+                                  case.q_len, d["tree_mask"], out)
+        else:
+            kb.kvattn_decode(h.h, d["q"], kcs[c], vcs[c], d["block_table"], d["seq_lens"],
+                             case.q_len, mask, case.n_sink, case.window, out)
 
     for w in range(a.warmup):
         step(w % copies)
@@ -243,8 +248,12 @@ def default_cpu_rows(case):
 
 def out_for_copy0(h, d, kcs, vcs, case, mask):
     out = torch.empty_like(d["q"])
-    kb.kvattn_decode(h.h, d["q"], kcs[0], vcs[0], d["block_table"], d["seq_lens"], case.q_len,
-                     mask, case.n_sink, case.window, out)
+    if case.mask_mode == "tree":
+        kb.kvattn_decode_tree(h.h, d["q"], kcs[0], vcs[0], d["block_table"], d["seq_lens"],
+                              case.q_len, d["tree_mask"], out)
+    else:
+        kb.kvattn_decode(h.h, d["q"], kcs[0], vcs[0], d["block_table"], d["seq_lens"],
+                         case.q_len, mask, case.n_sink, case.window, out)
     torch.cuda.synchronize()
     return out
 

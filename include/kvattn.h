@@ -27,6 +27,10 @@
  *   KVATTN_MASK_SINK_WINDOW  row at P sees p <= P with p < n_sink (attention sinks)
  *                            or p >= P - window + 1 (the `window` most recent
  *                            positions, its own included).
+ *   KVATTN_MASK_TREE         token-tree verification (kvattn_decode_tree): the q_len
+ *                            new positions P0 = T - q_len .. T - 1 are a tree of draft
+ *                            tokens; row i sees every p < P0 and P0 + j iff bit j
+ *                            of its mask word is set (its ancestors and itself).
  *
  * Layouts (row-major, head_dim innermost and contiguous; element type = dtype, or
  * kv_dtype for the caches):
@@ -84,7 +88,7 @@ enum kvattn_status {
 
 enum kvattn_dtype { KVATTN_F32 = 0, KVATTN_F16 = 1, KVATTN_BF16 = 2, KVATTN_FP8_E4M3 = 3 };
 enum kvattn_cache_mode { KVATTN_CONTIGUOUS = 0, KVATTN_PAGED = 1, KVATTN_RING = 2 };
-enum kvattn_mask_mode { KVATTN_MASK_CAUSAL = 0, KVATTN_MASK_SINK_WINDOW = 1 };
+enum kvattn_mask_mode { KVATTN_MASK_CAUSAL = 0, KVATTN_MASK_SINK_WINDOW = 1, KVATTN_MASK_TREE = 2 };
 enum kvattn_layout { KVATTN_LAYOUT_TOKEN_MAJOR = 0, KVATTN_LAYOUT_HEAD_MAJOR = 1 };
 
 typedef struct kvattn_config {
@@ -175,6 +179,22 @@ KVATTN_API int kvattn_append_decode(kvattn_handle* h, const void* q, const void*
                                     int32_t q_len, int32_t mask_mode, int32_t n_sink,
                                     int32_t window, void* out);
 
+/*
+ * Enqueue one decode step whose new rows form a token tree (SpecInfer verifies a
+ * tree of draft tokens in one pass with a tree-shaped attention mask - dothoosh.com
+ * speculative-decoding article; EAGLE-2 builds such trees dynamically - aioapex.com
+ * article): row i of sequence b sees every cached position before the new block
+ * (p < T - q_len) and new position T - q_len + j iff bit j of tree_mask[b * q_len + i]
+ * is set.  A row that sees nothing returns zeros.
+ *   tree_mask    [batch, q_len] uint64             device, read
+ *   q_len        1 .. min(max_q_len, 64); CONTIGUOUS or PAGED caches
+ * Other arguments and behaviour as kvattn_decode.
+ */
+KVATTN_API int kvattn_decode_tree(kvattn_handle* h, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t q_len,
+                                  const uint64_t* tree_mask, void* out);
+
 /* Free the workspace and the handle.  NULL is a no-op.  No enqueued decode may
  * still be using the handle. */
 KVATTN_API void kvattn_destroy(kvattn_handle* h);
@@ -223,6 +243,13 @@ KVATTN_API const char* kvattn_last_error(void);
 KVATTN_API int kvattn_debug_gather(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,
                         int32_t q_len, int32_t mask_mode, int32_t n_sink, int32_t window,
                         int32_t max_slots, int32_t* slots_out, int32_t* counts_out);
+
+/* Test entry: kvattn_debug_gather for a tree mask (tree_mask as for
+ * kvattn_decode_tree). */
+KVATTN_API int kvattn_debug_gather_tree(kvattn_handle* h, const int32_t* block_table,
+                                        const int32_t* seq_lens, int32_t q_len,
+                                        const uint64_t* tree_mask, int32_t max_slots,
+                                        int32_t* slots_out, int32_t* counts_out);
 
 #ifdef __cplusplus
 }

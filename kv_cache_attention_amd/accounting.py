@@ -32,7 +32,7 @@ def attended_span(mask_mode: str, T: int, q_len: int, n_sink: int, window: int):
     the union is [0, sink_count) + [tail_start, T)."""
     if T <= 0:
         return 0, 0, 0
-    if mask_mode == "causal":
+    if mask_mode in ("causal", "tree"):  # a tree's rows jointly see every position
         return 0, 0, T
     s = min(n_sink, T)
     w0 = max(T - q_len - window + 1, 0)

@@ -22,13 +22,13 @@ DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
                "fp8": torch.float8_e4m3fn}
 CACHE = {"contiguous": 0, "paged": 1, "ring": 2}
-MASK = {"causal": 0, "sink_window": 1}
+MASK = {"causal": 0, "sink_window": 1, "tree": 2}
 LAYOUT = {"token_major": 0, "head_major": 1}
 
 EXPORTS = ("kvattn_create", "kvattn_decode", "kvattn_destroy", "kvattn_set_stream",
            "kvattn_set_batch", "kvattn_set_split_len", "kvattn_set_kv_scales", "kvattn_plan",
            "kvattn_workspace_bytes", "kvattn_last_error", "kvattn_debug_gather", "kvattn_append",
-           "kvattn_append_decode")
+           "kvattn_append_decode", "kvattn_decode_tree", "kvattn_debug_gather_tree")
 
 
 class kvattn_config(ctypes.Structure):
@@ -83,6 +83,10 @@ def load() -> ctypes.CDLL:
     lib.kvattn_last_error.restype = ctypes.c_char_p
     lib.kvattn_debug_gather.argtypes = [H, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.kvattn_debug_gather.restype = ctypes.c_int
+    lib.kvattn_decode_tree.argtypes = [H, vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.kvattn_decode_tree.restype = ctypes.c_int
+    lib.kvattn_debug_gather_tree.argtypes = [H, vp, vp, i32, vp, i32, vp, vp]
+    lib.kvattn_debug_gather_tree.restype = ctypes.c_int
     lib.kvattn_append.argtypes = [H, vp, vp, vp, vp, vp, vp, i32, i32]
     lib.kvattn_append.restype = ctypes.c_int
     lib.kvattn_append_decode.argtypes = [H, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
@@ -131,6 +135,26 @@ def kvattn_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len: int, mas
                                 _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_table, "block_table"),
                                 _dev_ptr(seq_lens, "seq_lens"), q_len, mask_mode, n_sink, window,
                                 _dev_ptr(out, "out")), "kvattn_decode")
+
+
+def kvattn_decode_tree(h, q, k_cache, v_cache, block_table, seq_lens, q_len: int, tree_mask,
+                       out) -> None:
+    _check(load().kvattn_decode_tree(h, _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+                                     _dev_ptr(v_cache, "v_cache"),
+                                     _dev_ptr(block_table, "block_table"),
+                                     _dev_ptr(seq_lens, "seq_lens"), q_len,
+                                     _dev_ptr(tree_mask, "tree_mask"), _dev_ptr(out, "out")),
+           "kvattn_decode_tree")
+
+
+def kvattn_debug_gather_tree(h, block_table, seq_lens, q_len: int, tree_mask, max_slots: int,
+                             slots_out, counts_out) -> None:
+    _check(load().kvattn_debug_gather_tree(h, _dev_ptr(block_table, "block_table"),
+                                           _dev_ptr(seq_lens, "seq_lens"), q_len,
+                                           _dev_ptr(tree_mask, "tree_mask"), max_slots,
+                                           _dev_ptr(slots_out, "slots_out"),
+                                           _dev_ptr(counts_out, "counts_out")),
+           "kvattn_debug_gather_tree")
 
 
 def kvattn_append(h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len: int,
@@ -280,6 +304,31 @@ class KVAttn:
             want = TORCH_DTYPE[self.dtype] if name == "q" else TORCH_DTYPE[self.kv_dtype]
             if t.dtype != want:
                 raise ValueError(f"{name} must be {want}")
+
+    def decode_tree(self, q, k_cache, v_cache, block_table, seq_lens, q_len: int, tree_mask,
+                    out=None, stream: Optional[torch.cuda.Stream] = None):
+        """tree_mask: int64 device tensor [batch, q_len] of mask words (bit j = the row
+        attends new position j; bit 63 is the sign bit)."""
+        self._check_types(q=q, k_cache=k_cache, v_cache=v_cache)
+        if tree_mask.dtype != torch.int64:
+            raise ValueError("tree_mask must be int64 (uint64 words)")
+        if out is None:
+            out = torch.empty_like(q)
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        kvattn_set_stream(self.h, st.cuda_stream)
+        kvattn_decode_tree(self.h, q, k_cache, v_cache, block_table, seq_lens, q_len, tree_mask,
+                           out)
+        return out
+
+    def debug_gather_tree(self, block_table, seq_lens, q_len: int, tree_mask, max_slots: int,
+                          batch: int = 1):
+        dev = seq_lens.device
+        slots = torch.full((batch * q_len * max(max_slots, 1),), -2, dtype=torch.int32, device=dev)
+        counts = torch.zeros(batch * q_len, dtype=torch.int32, device=dev)
+        kvattn_set_stream(self.h, torch.cuda.current_stream(dev).cuda_stream)
+        kvattn_debug_gather_tree(self.h, block_table, seq_lens, q_len, tree_mask, max_slots,
+                                 slots, counts)
+        return slots.view(batch, q_len, max(max_slots, 1)), counts.view(batch, q_len)
 
     def append(self, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len: int,
                n_sink: int = 0, stream: Optional[torch.cuda.Stream] = None) -> None:

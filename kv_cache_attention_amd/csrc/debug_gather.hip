@@ -17,7 +17,7 @@ __global__ void debug_gather_kernel(const DecodeParams p, int max_slots, int32_t
     int32_t n = 0;
     for (int32_t j = 0; j < s.count; ++j) {
         const int32_t pos = span_pos(s, j);
-        if (!row_attends(p, s, i, pos)) continue;
+        if (!row_attends(p, s, b, i, pos)) continue;
         if (n < max_slots) {
             const Loc L = locate<CACHE>(p, s, b, pos);
             slots_out[(int64_t)row * max_slots + n] = (int32_t)flat_slot<CACHE>(p, L);

@@ -256,11 +256,16 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     // new row i sits at T - q_len + i; rows see positions <= their own
     const int32_t P0 = s.T - p.q_len;
     const bool sink_window = p.mask_mode == MASK_SINK_WINDOW;
+    // tree mask (token-tree verification): a row sees every position before the new
+    // block and new position P0 + j iff bit j of its word is set
+    const bool tree = p.mask_mode == MASK_TREE;
     int32_t hi[R], lo[R];
+    uint64_t tm[R];
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
-        hi[qt] = P0 + row_i[qt];
+        hi[qt] = tree ? s.T - 1 : P0 + row_i[qt];
         lo[qt] = sink_window ? hi[qt] - p.window + 1 : 0;
+        tm[qt] = tree ? p.tree_mask[(int64_t)b * p.q_len + row_i[qt]] : ~0ull;
     }
     const float c = p.scale_log2;
 
@@ -300,9 +305,11 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         load_k(j0 + nxt * TILE, kc);
 
         // Mask only where it can bite: a partial tile, rows that do not all see the
-        // tile's last position (q_len > 1), the window mask, or (paged) a bad entry.
+        // tile's last position (q_len > 1), a tile reaching a tree's new block, the
+        // window mask, or (paged) a bad entry.
         bool edge = (tb + TILE > j1) ||
-                    (p.q_len > 1 && (sink_window || span_pos(s, min(tb + TILE, j1) - 1) > P0));
+                    ((p.q_len > 1 || tree) &&
+                     (sink_window || span_pos(s, min(tb + TILE, j1) - 1) >= P0 + (tree ? 0 : 1)));
         if constexpr (CACHE == PAGED) edge = edge || __any(bad);
         if (edge) {
 #pragma unroll
@@ -316,10 +323,13 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
                         const int32_t blk = page_entry(p, b, pos);
                         pv = (uint32_t)blk < (uint32_t)p.num_blocks;
                     }
+                    const int32_t rel = pos - P0;
+                    const uint64_t bit = rel >= 0 ? 1ull << (rel & 63) : 0ull;
 #pragma unroll
                     for (int qt = 0; qt < R; ++qt) {
                         const bool ok = (j < j1) & pv & (pos <= hi[qt]) &
-                                        ((pos < p.n_sink) | (pos >= lo[qt]));
+                                        ((pos < p.n_sink) | (pos >= lo[qt])) &
+                                        ((rel < 0) | ((tm[qt] & bit) != 0));
                         st[tt][qt][e] = ok ? st[tt][qt][e] : NEG_INF;
                     }
                 }

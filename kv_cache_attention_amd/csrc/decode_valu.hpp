@@ -372,16 +372,23 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             vsc = p.v_scale[kvh];
         }
 
-        // MASKED: row r attends pos iff pos <= hi[r] and (pos < n_sink or pos >= lo[r])
+        // MASKED: row r attends pos iff pos <= hi[r] and (pos < n_sink or pos >= lo[r]);
+        // a tree mask (token-tree verification) instead lets row r see every position
+        // before the new block and new position P0 + j iff bit j of tm[r] is set
         int32_t hi[ROWS], lo[ROWS];
+        uint64_t tm[ROWS];
+        const bool tree = p.mask_mode == MASK_TREE;
+        const int32_t P0 = s.T - p.q_len;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
             const int rg = rb * ROWS + r;
             const int i = rg < p.rows ? rg / p.group : p.q_len - 1;
-            const int32_t P = s.T - p.q_len + i;
-            hi[r] = P;
+            const int32_t P = P0 + i;
+            hi[r] = tree ? s.T - 1 : P;
             lo[r] = p.mask_mode == MASK_SINK_WINDOW ? P - p.window + 1 : 0;
+            tm[r] = tree ? p.tree_mask[(int64_t)b * p.q_len + i] : ~0ull;
         }
+        const int32_t tree_from = tree ? P0 : 0x7fffffff;  // first position the tree masks
         float m[ROWS], l[ROWS], acc[ROWS][EPL];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -426,6 +433,22 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
                     if constexpr (MASKED)
                         ok = ok & (pos[u] <= hi[r]) & ((pos[u] < p.n_sink) | (pos[u] >= lo[r]));
                     sc[r][u] = ok ? x : NEG_INF;
+                }
+            }
+            if constexpr (MASKED) {
+                // the tree's bits, only on the (rare) tiles that reach the new block
+                bool reach = false;
+#pragma unroll
+                for (int u = 0; u < U; ++u) reach |= pos[u] >= tree_from;
+                if (__any(reach)) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int32_t rel = pos[u] - P0;
+                        const uint64_t bit = rel >= 0 ? 1ull << (rel & 63) : 0ull;
+#pragma unroll
+                        for (int r = 0; r < ROWS; ++r)
+                            if (rel >= 0 && !(tm[r] & bit)) sc[r][u] = NEG_INF;
+                    }
                 }
             }
             // a paged position behind an out-of-pool entry was read from block 0 and

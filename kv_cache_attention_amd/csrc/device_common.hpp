@@ -11,7 +11,7 @@ namespace kvattn {
 
 enum : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };  // FP8: OCP E4M3 codes
 enum : int { CONTIGUOUS = 0, PAGED = 1, RING = 2 };
-enum : int { MASK_CAUSAL = 0, MASK_SINK_WINDOW = 1 };
+enum : int { MASK_CAUSAL = 0, MASK_SINK_WINDOW = 1, MASK_TREE = 2 };
 
 // Everything a decode launch needs, passed by value as the kernel argument.
 struct DecodeParams {
@@ -41,6 +41,7 @@ struct DecodeParams {
     int32_t deterministic;  // waves take fixed tiles instead of a shared queue
     const float* k_scale; // 8-bit caches: [Hkv] dequantisation scales (else NULL)
     const float* v_scale;
+    const uint64_t* tree_mask;  // MASK_TREE: [batch, q_len] words, bit j = attends new position j
     float scale_log2;     // softmax scale * log2(e): scores are kept in the exp2 domain
 };
 
@@ -153,10 +154,15 @@ __device__ __forceinline__ int64_t flat_slot(const DecodeParams& p, const Loc& l
         return l.unit * p.capacity + l.idx;
 }
 
-// Does new row i (query position T - q_len + i) attend position pos?
-__device__ __forceinline__ bool row_attends(const DecodeParams& p, const SeqSpan& s, int i,
-                                            int32_t pos) {
-    const int32_t P = s.T - p.q_len + i;
+// Does new row i (query position T - q_len + i) of sequence b attend position pos?
+__device__ __forceinline__ bool row_attends(const DecodeParams& p, const SeqSpan& s, int b,
+                                            int i, int32_t pos) {
+    const int32_t P0 = s.T - p.q_len;
+    if (p.mask_mode == MASK_TREE) {
+        if (pos < P0) return true;
+        return pos < s.T && ((p.tree_mask[(int64_t)b * p.q_len + i] >> (pos - P0)) & 1);
+    }
+    const int32_t P = P0 + i;
     if (pos > P) return false;
     if (p.mask_mode == MASK_CAUSAL) return true;
     return pos < p.n_sink || pos >= P - p.window + 1;

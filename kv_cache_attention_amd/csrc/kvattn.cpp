@@ -177,8 +177,14 @@ int validate_decode_args(const kvattn_handle* h, int32_t q_len, int32_t mask_mod
     const kvattn_config& c = h->cfg;
     if (q_len < 1) return fail(KVATTN_ERR_INVALID_ARG, "q_len must be >= 1");
     if (q_len > c.max_q_len) return fail(KVATTN_ERR_CAPACITY, "q_len exceeds max_q_len");
-    if (mask_mode != KVATTN_MASK_CAUSAL && mask_mode != KVATTN_MASK_SINK_WINDOW)
+    if (mask_mode != KVATTN_MASK_CAUSAL && mask_mode != KVATTN_MASK_SINK_WINDOW &&
+        mask_mode != KVATTN_MASK_TREE)
         return fail(KVATTN_ERR_INVALID_ARG, "unknown mask_mode");
+    if (mask_mode == KVATTN_MASK_TREE) {
+        if (q_len > 64) return fail(KVATTN_ERR_INVALID_ARG, "tree mask: q_len must be <= 64");
+        if (c.cache_mode == KVATTN_RING)
+            return fail(KVATTN_ERR_UNSUPPORTED, "tree mask: contiguous or paged caches only");
+    }
     if (mask_mode == KVATTN_MASK_SINK_WINDOW) {
         if (n_sink < 0) return fail(KVATTN_ERR_INVALID_ARG, "n_sink must be >= 0");
         if (window < 1) return fail(KVATTN_ERR_INVALID_ARG, "window must be >= 1");
@@ -391,7 +397,7 @@ int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_si
 static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const void* q,
                         const void* k, const void* v, const int32_t* bt, const int32_t* sl,
                         int32_t q_len, int32_t mask_mode, int32_t n_sink, int32_t window,
-                        void* out, int min_chunk) {
+                        void* out, int min_chunk, const uint64_t* tree = nullptr) {
     const kvattn_config& c = h->cfg;
     p.q = q;
     p.k = k;
@@ -430,6 +436,7 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.deterministic = (c.flags & KVATTN_FLAG_DETERMINISTIC) ? 1 : 0;
     p.k_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->k_scale : nullptr;
     p.v_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->v_scale : nullptr;
+    p.tree_mask = mask_mode == KVATTN_MASK_TREE ? tree : nullptr;
     const float scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
 }
@@ -442,11 +449,13 @@ namespace {
 int prepare_decode(kvattn_handle* h, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,
                    int32_t mask_mode, int32_t n_sink, int32_t window, void* out,
-                   kvattn::DecodeParams& p, int* grid) {
+                   kvattn::DecodeParams& p, int* grid, const uint64_t* tree = nullptr) {
     *grid = 0;
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
     int rc = validate_decode_args(h, q_len, mask_mode, n_sink, window);
     if (rc) return rc;
+    if ((mask_mode == KVATTN_MASK_TREE) != (tree != nullptr))
+        return fail(KVATTN_ERR_INVALID_ARG, "a tree mask goes with kvattn_decode_tree (tree_mask non-NULL)");
     if (h->batch == 0) return KVATTN_OK;
     if (!q || !k_cache || !v_cache || !seq_lens || !out)
         return fail(KVATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, seq_lens and out must be non-NULL");
@@ -460,7 +469,7 @@ int prepare_decode(kvattn_handle* h, const void* q, const void* k_cache, const v
     rc = plan_for(h, q_len, mask_mode, n_sink, window, grid, &chunk);
     if (rc) return rc;
     fill_params(h, p, q, k_cache, v_cache, block_table, seq_lens, q_len, mask_mode, n_sink,
-                window, out, chunk);
+                window, out, chunk, tree);
     return KVATTN_OK;
 }
 
@@ -542,6 +551,18 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
     return launch_decode(h, p, grid, q_len);
 }
 
+int kvattn_decode_tree(kvattn_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,
+                       const uint64_t* tree_mask, void* out) {
+    kvattn::DecodeParams p;
+    int grid;
+    if (!tree_mask) return fail(KVATTN_ERR_INVALID_ARG, "tree_mask is NULL");
+    int rc = prepare_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len,
+                            KVATTN_MASK_TREE, 0, 0, out, p, &grid, tree_mask);
+    if (rc) return rc;
+    return launch_decode(h, p, grid, q_len);
+}
+
 int kvattn_append(kvattn_handle* h, const void* k_new, const void* v_new, void* k_cache,
                   void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                   int32_t q_len, int32_t n_sink) {
@@ -573,12 +594,19 @@ int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new, con
     return launch_decode(h, p, grid, q_len);
 }
 
-int kvattn_debug_gather(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,
-                        int32_t q_len, int32_t mask_mode, int32_t n_sink, int32_t window,
-                        int32_t max_slots, int32_t* slots_out, int32_t* counts_out) {
+}  // extern "C"
+
+namespace {
+
+int debug_gather(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,
+                 int32_t q_len, int32_t mask_mode, int32_t n_sink, int32_t window,
+                 const uint64_t* tree, int32_t max_slots, int32_t* slots_out,
+                 int32_t* counts_out) {
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
     int rc = validate_decode_args(h, q_len, mask_mode, n_sink, window);
     if (rc) return rc;
+    if ((mask_mode == KVATTN_MASK_TREE) != (tree != nullptr))
+        return fail(KVATTN_ERR_INVALID_ARG, "a tree mask needs its words (and only it)");
     if (h->batch == 0) return KVATTN_OK;
     if (!seq_lens || !slots_out || !counts_out || max_slots < 0)
         return fail(KVATTN_ERR_INVALID_ARG, "seq_lens, slots_out and counts_out must be non-NULL");
@@ -586,11 +614,30 @@ int kvattn_debug_gather(kvattn_handle* h, const int32_t* block_table, const int3
         return fail(KVATTN_ERR_INVALID_ARG, "block_table must be given exactly for a paged cache");
     kvattn::DecodeParams p;
     fill_params(h, p, nullptr, nullptr, nullptr, block_table, seq_lens, q_len, mask_mode, n_sink,
-                window, nullptr, 1 << 30);
+                window, nullptr, 1 << 30, tree);
     hipError_t e = kvattn::launch_debug_gather(p, max_slots, slots_out, counts_out, h->stream);
     if (e != hipSuccess)
         return fail(KVATTN_ERR_HIP, std::string("gather launch: ") + hipGetErrorString(e));
     return KVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_debug_gather(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t q_len, int32_t mask_mode, int32_t n_sink, int32_t window,
+                        int32_t max_slots, int32_t* slots_out, int32_t* counts_out) {
+    return debug_gather(h, block_table, seq_lens, q_len, mask_mode, n_sink, window, nullptr,
+                        max_slots, slots_out, counts_out);
+}
+
+int kvattn_debug_gather_tree(kvattn_handle* h, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t q_len, const uint64_t* tree_mask,
+                             int32_t max_slots, int32_t* slots_out, int32_t* counts_out) {
+    if (!tree_mask) return fail(KVATTN_ERR_INVALID_ARG, "tree_mask is NULL");
+    return debug_gather(h, block_table, seq_lens, q_len, KVATTN_MASK_TREE, 0, 0, tree_mask,
+                        max_slots, slots_out, counts_out);
 }
 
 }  // extern "C"

@@ -38,6 +38,7 @@ import dataclasses
 from dataclasses import dataclass
 from typing import Optional, Tuple
 
+import numpy as np
 import torch
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
@@ -57,7 +58,7 @@ class Case:
     cache_mode: str                 # "contiguous" | "paged" | "ring"
     capacity: int                   # slots per sequence (paged: blocks_per_seq * block_size)
     q_len: int = 1
-    mask_mode: str = "causal"       # "causal" | "sink_window"
+    mask_mode: str = "causal"       # "causal" | "sink_window" | "tree"
     n_sink: int = 0
     window: int = 0
     block_size: int = 16
@@ -109,8 +110,29 @@ DECODE_7B_FP8 = DECODE_7B.replace(name="decode_7b_fp8", seed=6, kv_dtype="fp8")
 SINK_WINDOW_FP8 = SINK_WINDOW.replace(name="sink_window_fp8", seed=7, kv_dtype="fp8")
 PAGED_100K_FP8 = PAGED_100K.replace(name="paged_100k_fp8", seed=8, kv_dtype="fp8")
 
+# Token-tree verification: the verify step with 8 draft tokens per sequence arranged
+# as a seeded random tree (8 x GQA 8 = 64 rows per KV head).
+TREE_VERIFY = SPEC_VERIFY.replace(name="tree_verify", seed=9, q_len=8, mask_mode="tree")
+
 CONFIGS = {c.name: c for c in (TINY, DECODE_7B, SPEC_VERIFY, SINK_WINDOW, PAGED_100K,
-                               DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8)}
+                               DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8, TREE_VERIFY)}
+
+
+def tree_words_from_parents(parents) -> list:
+    """Mask words of a token tree given each node's parent (-1: a child of the last
+    cached token; parents precede their children): bit j of node i's word is set iff
+    node j is node i or one of its ancestors."""
+    words = []
+    for i, par in enumerate(parents):
+        assert par < i
+        words.append((words[par] if par >= 0 else 0) | (1 << i))
+    return words
+
+
+def draw_tree(q_len: int, g: torch.Generator) -> list:
+    """A seeded random tree of q_len draft tokens: node 0 hangs off the cached prefix,
+    node j > 0 off a node drawn uniformly from 0 .. j - 1; returns the parents."""
+    return [-1] + [int(torch.randint(0, j, (1,), generator=g)) for j in range(1, q_len)]
 
 
 def cache_shape(case: Case) -> Tuple[int, ...]:
@@ -145,6 +167,11 @@ def make_inputs(case: Case, device: str = "cpu") -> dict:
         assert case.capacity % case.block_size == 0 and need <= case.num_blocks
         perm = torch.randperm(case.num_blocks, generator=g_cpu)
         block_table = perm[:need].view(case.batch, case.blocks_per_seq).to(torch.int32).contiguous()
+    tree_mask = None
+    if case.mask_mode == "tree":
+        # one tree per sequence, as int64 words (bit 63 would be the sign bit)
+        words = [tree_words_from_parents(draw_tree(case.q_len, g_cpu)) for _ in range(case.batch)]
+        tree_mask = torch.tensor(np.array(words, dtype=np.uint64).view(np.int64))
 
     # 2. values (float32 standard normals)
     if device == "cpu":
@@ -182,8 +209,26 @@ def make_inputs(case: Case, device: str = "cpu") -> dict:
         del x
     out["seq_lens"] = seq_lens.to(device)
     out["block_table"] = block_table.to(device) if block_table is not None else None
+    out["tree_mask"] = tree_mask.to(device) if tree_mask is not None else None
     out["case"] = case
     return out
+
+
+def small_tree_variants():
+    """Reduced token-tree verification cases: 5 and 8 draft tokens with GQA 8 (40 and
+    64 rows per KV head: matrix-core kernel), 6 tokens without GQA and 7 tokens on a
+    paged cache with GQA 4 (vector-ALU kernel), and sequences shorter than their tree."""
+    sv = small_variants()
+    base = sv["spec_verify_small"].replace(mask_mode="tree")
+    return {
+        "tree_small": base.replace(name="tree_small", seed=31),
+        "tree_small_q8": base.replace(name="tree_small_q8", q_len=8, seed=32),
+        "tree_short": base.replace(name="tree_short", q_len=8, seq_lens=(1000, 3, 8), seed=33),
+        "tree_valu": sv["decode_7b_small"].replace(name="tree_valu", mask_mode="tree",
+                                                   q_len=6, seq_len_range=(1, 1200), seed=34),
+        "tree_paged": sv["paged_small"].replace(name="tree_paged", mask_mode="tree", q_len=7,
+                                                seed=35),
+    }
 
 
 def small_fp8_variants():

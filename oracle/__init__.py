@@ -14,5 +14,5 @@ append (the new rows written to their cache slots) that precedes a decode.
 from .oracle import (  # noqa: F401
     DTYPE_CODES, CACHE_CODES, MASK_CODES, load, decode, decode_rows, attended,
     decode_np, attended_positions_np, slot_np, full_causal_np, tiled_softmax_dot_np,
-    split_merge_np, to_f64, threads, append_np,
+    split_merge_np, to_f64, threads, append_np, tree_words,
 )

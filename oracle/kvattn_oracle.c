@@ -34,6 +34,12 @@
  *  - paged slot: block_table[b][p / block_size] * block_size + p % block_size
  *    (lesson, "PagedAttention": 16-token blocks, a page table from logical
  *    positions to physical blocks).
+ *  - tree mask (token-tree verification: SpecInfer verifies a tree of draft
+ *    tokens with a custom attention mask, speculative-decoding article; EAGLE-2
+ *    grows such trees, aioapex.com article): the q_len new positions
+ *    P0 .. P0 + q_len - 1 (P0 = T - q_len) are the tree's tokens; row i sees every
+ *    earlier cached position p < P0 and the new position P0 + j exactly when bit j
+ *    of its mask word is set (its ancestors and itself).
  *
  * Storage formats are decoded from their bit definitions (IEEE binary16,
  * bfloat16 = the top half of binary32, OCP 8-bit E4M3), exactly, into double.
@@ -55,7 +61,7 @@
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_FP8_E4M3 = 3 };
 enum { OR_CONTIGUOUS = 0, OR_PAGED = 1, OR_RING = 2 };
-enum { OR_CAUSAL = 0, OR_SINK_WINDOW = 1 };
+enum { OR_CAUSAL = 0, OR_SINK_WINDOW = 1, OR_TREE = 2 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 static double f16_to_f64(uint16_t h) {
@@ -117,6 +123,15 @@ int oracle_attends(int mask_mode, int64_t P, int64_t p, int n_sink, int window) 
     return (p < n_sink) || (p >= P - window + 1);  /* sinks, or inside the trailing window */
 }
 
+/* Tree mask: does a new row with mask word `bits` attend position p of a sequence
+ * whose new block starts at P0 and holds q_len positions? */
+int oracle_attends_tree(int64_t P0, int q_len, uint64_t bits, int64_t p) {
+    if (p < 0) return 0;
+    if (p < P0) return 1;                          /* the cached prefix */
+    if (p >= P0 + q_len) return 0;
+    return (int)((bits >> (p - P0)) & 1u);         /* an ancestor in the tree, or itself */
+}
+
 /* Flat slot (row of the [slots, Hkv, d] view of the cache) holding position p
  * of sequence b.  Returns -1 when the position has no slot. */
 int64_t oracle_slot(int cache_mode, int b, int64_t p, int capacity, int block_size,
@@ -142,12 +157,14 @@ int64_t oracle_slot(int cache_mode, int b, int64_t p, int capacity, int block_si
  * returns the total count. */
 int64_t oracle_attended(int cache_mode, int mask_mode, int b, int i, int q_len, int64_t T,
                         int n_sink, int window, int capacity, int block_size,
-                        const int32_t* block_table, int blocks_per_seq,
+                        const int32_t* block_table, int blocks_per_seq, uint64_t tree_bits,
                         int64_t* pos_out, int64_t* slot_out, int64_t max_out) {
     int64_t P = T - q_len + i;
     int64_t n = 0;
     for (int64_t p = 0; p < T; ++p) {
-        if (!oracle_attends(mask_mode, P, p, n_sink, window)) continue;
+        const int att = mask_mode == OR_TREE ? oracle_attends_tree(T - q_len, q_len, tree_bits, p)
+                                             : oracle_attends(mask_mode, P, p, n_sink, window);
+        if (!att) continue;
         if (n < max_out) {
             if (pos_out) pos_out[n] = p;
             if (slot_out)
@@ -167,6 +184,7 @@ typedef struct {
     int kv_dtype;                 /* element type of the caches; dtype when equal */
     const float* k_scale;         /* [num_kv_heads] dequantisation scales, or NULL (1) */
     const float* v_scale;
+    const uint64_t* tree_mask;    /* OR_TREE: [batch, q_len] mask words, else unused */
 } oracle_problem;
 
 /* One output row: out[d] for (b, i, h).  Returns the number of attended
@@ -178,9 +196,12 @@ static int64_t decode_one_row(const oracle_problem* pr, const void* q, const voi
     const int g = pr->num_q_heads / pr->num_kv_heads;
     const int kvh = h / g;
     const double scale = pr->scale != 0.0 ? pr->scale : 1.0 / sqrt((double)D);
+    const uint64_t bits =
+        pr->mask_mode == OR_TREE ? pr->tree_mask[(int64_t)b * pr->q_len + i] : 0;
     const int64_t n = oracle_attended(pr->cache_mode, pr->mask_mode, b, i, pr->q_len, T,
                                       pr->n_sink, pr->window, pr->capacity, pr->block_size,
-                                      block_table, pr->blocks_per_seq, NULL, slots, INT64_MAX);
+                                      block_table, pr->blocks_per_seq, bits, NULL, slots,
+                                      INT64_MAX);
     for (int d = 0; d < D; ++d) out[d] = 0.0;
     if (n == 0) return 0;
     const int64_t qbase = (((int64_t)b * pr->q_len + i) * pr->num_q_heads + h) * D;
@@ -229,6 +250,8 @@ int oracle_decode_rows(const oracle_problem* pr, const void* q, const void* k_ca
                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                        const int32_t* rows, int64_t n_rows, double* out, int n_threads) {
     if (!pr || pr->num_kv_heads <= 0 || pr->num_q_heads % pr->num_kv_heads) return -1;
+    if (pr->mask_mode == OR_TREE && (pr->cache_mode == OR_RING || !pr->tree_mask || pr->q_len > 64))
+        return -1;
     if (pr->cache_mode == OR_RING) {
         /* every position a row can attend must still be live in the ring */
         if (pr->mask_mode != OR_SINK_WINDOW || pr->window < 1 ||

@@ -32,7 +32,7 @@ import torch
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 CACHE_CODES = {"contiguous": 0, "paged": 1, "ring": 2}
-MASK_CODES = {"causal": 0, "sink_window": 1}
+MASK_CODES = {"causal": 0, "sink_window": 1, "tree": 2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -46,7 +46,8 @@ class _Problem(ctypes.Structure):
         "mask_mode", "n_sink", "window")] + [("scale", ctypes.c_double),
                                              ("kv_dtype", ctypes.c_int),
                                              ("k_scale", ctypes.c_void_p),
-                                             ("v_scale", ctypes.c_void_p)]
+                                             ("v_scale", ctypes.c_void_p),
+                                             ("tree_mask", ctypes.c_void_p)]
 
 
 def load():
@@ -67,7 +68,7 @@ def load():
                                        ctypes.c_int]
     lib.oracle_decode_rows.restype = ctypes.c_int
     lib.oracle_attended.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int64] + [ctypes.c_int] * 4 + [
-        i32p, ctypes.c_int, i64p, i64p, ctypes.c_int64]
+        i32p, ctypes.c_int, ctypes.c_uint64, i64p, i64p, ctypes.c_int64]
     lib.oracle_attended.restype = ctypes.c_int64
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_decode_elem.argtypes = [vp, ctypes.c_int, ctypes.c_int64]
@@ -85,13 +86,30 @@ def kv_dtype_of(pr) -> str:
     return getattr(pr, "kv_dtype", None) or pr.dtype
 
 
-def _problem(pr, scale: float = 0.0, k_scale=None, v_scale=None) -> _Problem:
-    # k_scale / v_scale: float32 CPU tensors [num_kv_heads] kept alive by the caller
+def _problem(pr, scale: float = 0.0, k_scale=None, v_scale=None, tree=None) -> _Problem:
+    # k_scale / v_scale: float32 CPU tensors [num_kv_heads], tree: int64 CPU tensor
+    # [batch, q_len] of mask words; kept alive by the caller
     return _Problem(DTYPE_CODES[pr.dtype], pr.batch, pr.num_q_heads, pr.num_kv_heads,
                     pr.head_dim, pr.q_len, CACHE_CODES[pr.cache_mode], pr.capacity,
                     pr.block_size, pr.capacity // pr.block_size, MASK_CODES[pr.mask_mode],
                     pr.n_sink, pr.window, float(scale), DTYPE_CODES[kv_dtype_of(pr)],
-                    _ptr(k_scale), _ptr(v_scale))
+                    _ptr(k_scale), _ptr(v_scale), _ptr(tree))
+
+
+def tree_words(tree_mask) -> np.ndarray:
+    """Mask words as uint64 (bit j = the row attends new position j); accepts int64
+    torch tensors (bit 63 as the sign) or any integer array."""
+    if isinstance(tree_mask, torch.Tensor):
+        return np.ascontiguousarray(_cpu(tree_mask).to(torch.int64).numpy().view(np.uint64))
+    a = np.asarray(tree_mask)
+    return np.ascontiguousarray(a.view(np.uint64) if a.dtype == np.int64 else a.astype(np.uint64))
+
+
+def _tree(tree_mask):
+    """Mask words as a contiguous int64 CPU tensor for the C oracle."""
+    if tree_mask is None:
+        return None
+    return torch.from_numpy(tree_words(tree_mask).view(np.int64).copy())
 
 
 def _scales(k_scale, v_scale):
@@ -116,14 +134,16 @@ def _ptr(t, ctype=None):
 
 
 def decode(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0,
-           n_threads: int = 0, k_scale=None, v_scale=None) -> np.ndarray:
+           n_threads: int = 0, k_scale=None, v_scale=None, tree_mask=None) -> np.ndarray:
     """All rows; float64 [batch, q_len, num_q_heads, head_dim].  An 8-bit cache
-    (pr.kv_dtype == "fp8") takes per-KV-head dequantisation scales k_scale, v_scale."""
+    (pr.kv_dtype == "fp8") takes per-KV-head dequantisation scales k_scale, v_scale;
+    pr.mask_mode == "tree" takes tree_mask [batch, q_len] (uint64 words)."""
     lib = load()
     q, kc, vc, bt, sl = (_cpu(x) for x in (q, k_cache, v_cache, block_table, seq_lens))
     ks, vs = _scales(k_scale, v_scale)
+    tm = _tree(tree_mask)
     out = np.zeros((pr.batch, pr.q_len, pr.num_q_heads, pr.head_dim), np.float64)
-    rc = lib.oracle_decode(ctypes.byref(_problem(pr, scale, ks, vs)), _ptr(q), _ptr(kc), _ptr(vc),
+    rc = lib.oracle_decode(ctypes.byref(_problem(pr, scale, ks, vs, tm)), _ptr(q), _ptr(kc), _ptr(vc),
                            _ptr(bt, ctypes.c_int32), _ptr(sl, ctypes.c_int32),
                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), n_threads)
     if rc != 0:
@@ -132,14 +152,15 @@ def decode(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0,
 
 
 def decode_rows(pr, q, k_cache, v_cache, block_table, seq_lens, rows, scale: float = 0.0,
-                n_threads: int = 0, k_scale=None, v_scale=None) -> np.ndarray:
+                n_threads: int = 0, k_scale=None, v_scale=None, tree_mask=None) -> np.ndarray:
     """Listed rows only: rows is int [n, 3] of (b, i, h); returns float64 [n, head_dim]."""
     lib = load()
     q, kc, vc, bt, sl = (_cpu(x) for x in (q, k_cache, v_cache, block_table, seq_lens))
     ks, vs = _scales(k_scale, v_scale)
+    tm = _tree(tree_mask)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
     out = np.zeros((rows.shape[0], pr.head_dim), np.float64)
-    rc = lib.oracle_decode_rows(ctypes.byref(_problem(pr, scale, ks, vs)), _ptr(q), _ptr(kc), _ptr(vc),
+    rc = lib.oracle_decode_rows(ctypes.byref(_problem(pr, scale, ks, vs, tm)), _ptr(q), _ptr(kc), _ptr(vc),
                                 _ptr(bt, ctypes.c_int32), _ptr(sl, ctypes.c_int32),
                                 rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                 rows.shape[0],
@@ -149,19 +170,21 @@ def decode_rows(pr, q, k_cache, v_cache, block_table, seq_lens, rows, scale: flo
     return out
 
 
-def attended(pr, block_table, seq_lens, b: int, i: int):
-    """(positions, flat slots) that row (b, i) attends, in increasing position order."""
+def attended(pr, block_table, seq_lens, b: int, i: int, tree_bits: int = 0):
+    """(positions, flat slots) that row (b, i) attends, in increasing position order
+    (mask "tree": tree_bits is the row's mask word)."""
     lib = load()
     bt, sl = _cpu(block_table), _cpu(seq_lens)
     T = int(sl[b])
     n = lib.oracle_attended(CACHE_CODES[pr.cache_mode], MASK_CODES[pr.mask_mode], b, i,
                             pr.q_len, T, pr.n_sink, pr.window, pr.capacity, pr.block_size,
-                            _ptr(bt, ctypes.c_int32), pr.capacity // pr.block_size, None, None, 0)
+                            _ptr(bt, ctypes.c_int32), pr.capacity // pr.block_size, tree_bits,
+                            None, None, 0)
     pos = np.zeros(max(n, 1), np.int64)
     slots = np.zeros(max(n, 1), np.int64)
     lib.oracle_attended(CACHE_CODES[pr.cache_mode], MASK_CODES[pr.mask_mode], b, i, pr.q_len, T,
                         pr.n_sink, pr.window, pr.capacity, pr.block_size,
-                        _ptr(bt, ctypes.c_int32), pr.capacity // pr.block_size,
+                        _ptr(bt, ctypes.c_int32), pr.capacity // pr.block_size, tree_bits,
                         pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                         slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n)
     return pos[:n], slots[:n]
@@ -180,10 +203,17 @@ def to_f64(t) -> np.ndarray:
 
 
 def attended_positions_np(mask_mode: str, T: int, q_len: int, i: int, n_sink: int,
-                          window: int) -> np.ndarray:
-    """Positions the new row i (at T - q_len + i) attends, as a boolean mask over [0, T)."""
+                          window: int, tree_bits: int = 0) -> np.ndarray:
+    """Positions the new row i (at T - q_len + i) attends, in increasing order.  Tree
+    mask: every position before the new block, and new position T - q_len + j when
+    bit j of tree_bits is set."""
     P = T - q_len + i
     p = np.arange(max(T, 0), dtype=np.int64)
+    if mask_mode == "tree":
+        j = p - (T - q_len)
+        bit = np.array([(int(tree_bits) >> int(x)) & 1 if 0 <= x < 64 else 0 for x in j],
+                       dtype=bool) if p.size else np.zeros(0, bool)
+        return p[(j < 0) | bit]
     keep = p <= P
     if mask_mode == "sink_window":
         keep &= (p < n_sink) | (p > P - window)
@@ -205,7 +235,7 @@ def slot_np(cache_mode: str, b: int, p: np.ndarray, capacity: int, block_size: i
 
 
 def decode_np(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0,
-              k_scale=None, v_scale=None) -> np.ndarray:
+              k_scale=None, v_scale=None, tree_mask=None) -> np.ndarray:
     """float64 [batch, q_len, Hq, D]; gathers only the attended slots.  8-bit caches
     are dequantised with the per-KV-head scales (torch's E4M3 conversion)."""
     D, Hq, Hkv = pr.head_dim, pr.num_q_heads, pr.num_kv_heads
@@ -221,8 +251,9 @@ def decode_np(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0
     kv_of_h = np.arange(Hq) // g
     for b in range(pr.batch):
         for i in range(pr.q_len):
+            bits = 0 if tree_mask is None else int(tree_words(tree_mask)[b, i])
             pos = attended_positions_np(pr.mask_mode, int(sl[b]), pr.q_len, i, pr.n_sink,
-                                        pr.window)
+                                        pr.window, bits)
             if pos.size == 0:
                 continue
             slots = slot_np(pr.cache_mode, b, pos, pr.capacity, pr.block_size, block_table,

@@ -15,9 +15,11 @@ REL_L2 = {"f32": 1e-6, "f16": 2e-3, "bf16": 1e-2}
 def attended_union_slots(case, inp):
     """Flat slots any new row of any sequence attends (from the oracle's enumerator)."""
     used = set()
+    words = oracle.tree_words(inp["tree_mask"]) if inp.get("tree_mask") is not None else None
     for b in range(case.batch):
         for i in range(case.q_len):
-            _, slots = oracle.attended(case, inp["block_table"], inp["seq_lens"], b, i)
+            bits = int(words[b, i]) if words is not None else 0
+            _, slots = oracle.attended(case, inp["block_table"], inp["seq_lens"], b, i, bits)
             used.update(slots.tolist())
     return used
 
@@ -63,8 +65,12 @@ def run(case, dinp, layout="token_major", split_len=0, q=None, handle=None):
     kc, vc = dinp["k_cache"], dinp["v_cache"]
     if layout == "head_major":
         kc, vc = to_head_major(case, kc), to_head_major(case, vc)
-    out = h.decode(dinp["q"] if q is None else q, kc, vc, dinp["block_table"], dinp["seq_lens"],
-                   case.q_len, case.mask_mode, case.n_sink, case.window)
+    if case.mask_mode == "tree":
+        out = h.decode_tree(dinp["q"] if q is None else q, kc, vc, dinp["block_table"],
+                            dinp["seq_lens"], case.q_len, dinp["tree_mask"])
+    else:
+        out = h.decode(dinp["q"] if q is None else q, kc, vc, dinp["block_table"],
+                       dinp["seq_lens"], case.q_len, case.mask_mode, case.n_sink, case.window)
     torch.cuda.synchronize()
     return out
 

@@ -517,9 +517,14 @@ def test_step_bytes_count_oracle_attended_union(name):
         bt = None
         if case.cache_mode == "paged":
             bt = torch.arange(case.blocks_per_seq, dtype=torch.int32).view(1, -1)
+        words = [0] * case.q_len
+        if case.mask_mode == "tree":  # any tree: every node sees itself
+            words = workloads.tree_words_from_parents(
+                workloads.draw_tree(case.q_len, torch.Generator().manual_seed(T)))
         union = set()
         for i in range(case.q_len):
-            pos, _ = oracle.attended(one, bt, torch.tensor([T], dtype=torch.int32), 0, i)
+            pos, _ = oracle.attended(one, bt, torch.tensor([T], dtype=torch.int32), 0, i,
+                                     words[i])
             union.update(pos.tolist())
         assert accounting.attended_count(case.mask_mode, T, case.q_len, case.n_sink,
                                          case.window) == len(union)
