@@ -31,6 +31,7 @@ from kv_cache_attention_amd import binding as kb  # noqa: E402
 
 METRIC = "decode-attention effective HBM GB/s (% of MI355X peak) and µs/step, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense matrix-core peaks, MI355X
 MALL_BYTES = 256 << 20
 COPY_BYTES = 1 << 30   # plain copy of known size, the yardstick for the traffic counters
 PROFILES = os.path.join(ROOT, "profiles")
@@ -123,6 +124,12 @@ def main():
     sl_host = d["seq_lens"].cpu().tolist()
     step_bytes = accounting.step_bytes(case, sl_host)
     step_flops = accounting.step_flops(case, sl_host)
+    # multiply-adds the rows really do (row by row; the union count above is an upper
+    # bound): decides whether the step is bound by the matrix cores or by HBM
+    row_flops = (4 * case.head_dim * accounting.attended_pairs(case, sl_host)
+                 if case.mask_mode != "tree" else step_flops)
+    mfma_bound = (case.dtype in MFMA_PEAK_TFLOPS and row_flops / step_bytes >
+                  MFMA_PEAK_TFLOPS[case.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9))
     kv_attended = step_bytes - 2 * case.batch * case.q_len * case.num_q_heads * case.head_dim * \
         accounting.ELEM_BYTES[case.dtype]
 
@@ -214,6 +221,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "row_flops_per_step": row_flops,
             "traffic": measured_traffic(case.name, a.layout),
             "bytes_per_step": step_bytes,
             "flops_per_step": step_flops,
@@ -223,6 +231,12 @@ def main():
                      "HIP events on the library's stream",
         },
     }
+    if mfma_bound:  # the matrix cores bound this step: flops per launch against their peak
+        tf = row_flops / (ev_mean * 1e-3) / 1e12
+        rec["roofline"].update({"bound": "mfma", "achieved": round(tf, 2),
+                                "peak": MFMA_PEAK_TFLOPS[case.dtype], "unit": "TFLOP/s",
+                                "frac": round(tf / MFMA_PEAK_TFLOPS[case.dtype], 4),
+                                "hbm_gbs": round(achieved, 2)})
     # yardstick for the memory counters: one plain device copy of known size
     # (outside the timed region; a profiler run scales FETCH/WRITE_SIZE by it)
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)

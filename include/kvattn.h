@@ -10,7 +10,10 @@
  * and Flash Attention": each new token is one query against the cached keys).
  * q_len = 1 is plain autoregressive decode; q_len = 1 + k is the verification
  * pass of speculative decoding, where every new row sees all earlier positions
- * (dothoosh.com speculative-decoding article, "verify phase").
+ * (dothoosh.com speculative-decoding article, "verify phase"); q_len in the
+ * hundreds is a chunk of a prefill against the cached prefix (the lesson's
+ * FlashAttention section: query tiles against key/value tiles, softmax kept
+ * running), the rows then run in blocks of 64 on the matrix cores.
  *
  * Cache forms:
  *   CONTIGUOUS  each sequence owns `capacity` consecutive slots; position p is slot p.
@@ -97,7 +100,7 @@ typedef struct kvattn_config {
     int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
     int32_t head_dim;       /* 64 or 128 */
     int32_t max_batch;      /* >= 1 */
-    int32_t max_q_len;      /* 1 .. 64 */
+    int32_t max_q_len;      /* 1 .. 1024 (token-tree masks: q_len <= 64) */
     int32_t cache_mode;     /* kvattn_cache_mode */
     int32_t capacity;       /* CONTIGUOUS / RING: slots per sequence; PAGED: positions per
                                sequence = block_size * (row length of block_table) */

@@ -71,6 +71,23 @@ def step_bytes(case, seq_lens: Sequence[int]) -> int:
     return total + 2 * qo + 4 * case.batch + scales
 
 
+def attended_pairs(case, seq_lens: Sequence[int]) -> int:
+    """(query row, attended position) pairs of a step with the causal or sink/window mask,
+    counted row by row (row i of a sequence of T positions sits at T - q_len + i)."""
+    n = 0
+    for T in seq_lens:
+        T = int(T)
+        for i in range(case.q_len):
+            P = T - case.q_len + i
+            if P < 0:
+                continue
+            if case.mask_mode == "sink_window":
+                n += min(case.n_sink, P + 1) + max(0, P + 1 - max(case.n_sink, P - case.window + 1))
+            else:
+                n += P + 1
+    return n * case.num_q_heads
+
+
 def step_flops(case, seq_lens: Sequence[int]) -> int:
     n = sum(attended_count(case.mask_mode, int(T), case.q_len, case.n_sink, case.window)
             for T in seq_lens)

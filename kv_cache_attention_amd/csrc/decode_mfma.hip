@@ -139,7 +139,10 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
     for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
     const int b = pc.b;
-    const int kvh = pc.seg;
+    // more rows than one block holds (chunked prefill: hundreds of new rows) are cut
+    // into blocks of NQ rows, one segment each
+    const int kvh = pc.seg / p.row_blocks;
+    const int row0 = (pc.seg - kvh * p.row_blocks) * NQ;
     const int32_t j0 = pc.ja;
     const int32_t j1 = pc.jb;
 
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     int row_i[R];
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
-        const int n = qt * 16 + lr;
+        const int n = row0 + qt * 16 + lr;
         row_i[qt] = n < p.rows ? n / p.group : p.q_len - 1;
     }
 
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         const int idx = tid + k * MFMA_THREADS;
         const int f = idx / 64, ll = idx % 64;
         const int qt = f / KS, ks = f % KS;
-        const int n = qt * 16 + ll % 16;
+        const int n = row0 + qt * 16 + ll % 16;
         qreg[k] = u32x4{0, 0, 0, 0};
         if (idx < G::QFRAGS * 64 && n < p.rows) {
             const int i = n / p.group;
@@ -436,7 +439,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     for (int idx = tid; idx < NQ * D / 4; idx += MFMA_THREADS) {
         const int n = idx / (D / 4);
         const int d = (idx - n * (D / 4)) * 4;
-        if (n >= p.rows) continue;
+        if (row0 + n >= p.rows) continue;
         float M = NEG_INF;
 #pragma unroll
         for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, sm_m[w][n]);
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             A.z += f * a.z;
             A.w += f * a.w;
         }
-        const int64_t rid = row_id_of(p, b, kvh, n);
+        const int64_t rid = row_id_of(p, b, kvh, row0 + n);
         if (pc.nparts == 1) {
             const float inv = L > 0.0f ? 1.0f / L : 0.0f;
             const uint2 w = {pack2<DT>(A.x * inv, A.y * inv), pack2<DT>(A.z * inv, A.w * inv)};
@@ -469,7 +472,8 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     __syncthreads();
     if (pc.nparts > 1) {
         auto& msm = *reinterpret_cast<MergeSmem<NQ, MFMA_THREADS>*>(smem);
-        arrive_and_merge<DT, D, NQ, MFMA_THREADS>(p, b, kvh, 0, pc.unit, pc.slot0, pc.nparts, msm);
+        arrive_and_merge<DT, D, NQ, MFMA_THREADS>(p, b, kvh, row0, pc.unit, pc.slot0, pc.nparts,
+                                                  msm);
         __syncthreads();  // LDS is reused by the next piece
     }
     });
@@ -477,10 +481,11 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     zero_empty_sequences<DT, MFMA_THREADS, D>(p, wg, n_wg);
 }
 
+// 16 rows or more per KV head; above 64 the rows run in blocks of 64 (4 row tiles).
 bool mfma_supported(int dtype, int head_dim, int rows) {
-    return (dtype == F16 || dtype == BF16) && (head_dim == 64 || head_dim == 128) &&
-           rows >= 16 && rows <= 64;
+    return (dtype == F16 || dtype == BF16) && (head_dim == 64 || head_dim == 128) && rows >= 16;
 }
+int mfma_rows_per_block(int rows) { return rows <= 64 ? (rows + 15) / 16 * 16 : 64; }
 
 template <int DT, int D, int R>
 static const void* mfma_kernel_c(int cache_mode) {

@@ -51,7 +51,7 @@ static_assert(kTailPct >= 0 && kTailPct < 100 && kTailUnits >= 1, "tail shape");
 constexpr int kMinChunk = 256;
 constexpr int kMinChunkMfma = 512;
 constexpr int kChunkQuantum = 64;
-constexpr int kMaxQLen = 64;
+constexpr int kMaxQLen = 1024;  // chunked prefill: hundreds of new rows per sequence
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -69,7 +69,7 @@ struct kvattn_handle {
     kvattn_config cfg;
     int device;
     int num_cus;
-    int resident[65];       // per q_len: workgroups of its kernel instance resident at once
+    int resident[kMaxQLen + 1];  // per q_len: workgroups of its kernel instance resident at once
     hipStream_t stream;
     int32_t batch;
     int32_t forced_chunk;
@@ -104,19 +104,18 @@ bool use_mfma(const kvattn_config& c, int q_len) {
     return kv_dtype_of(c) == c.dtype && kvattn::mfma_supported(c.dtype, c.head_dim, rows_of(c, q_len));
 }
 
-int row_blocks_of(const kvattn_config& c, int q_len) {
-    if (use_mfma(c, q_len)) return 1;
-    const int rows = rows_of(c, q_len);
-    const int rpb = kvattn::valu_rows_per_block(rows);
-    return (rows + rpb - 1) / rpb;
-}
-
 // Rows of one segment as laid out in the workspace (the kernel instance's row block;
-// the matrix-core kernel pads to whole 16-row tiles).
+// the matrix-core kernel pads to whole 16-row tiles, at most 64 rows a block).
 int seg_rows_of(const kvattn_config& c, int q_len) {
     const int rows = rows_of(c, q_len);
-    if (use_mfma(c, q_len)) return (rows + 15) / 16 * 16;
+    if (use_mfma(c, q_len)) return kvattn::mfma_rows_per_block(rows);
     return kvattn::valu_rows_per_block(rows);
+}
+
+int row_blocks_of(const kvattn_config& c, int q_len) {
+    const int rows = rows_of(c, q_len);
+    const int rpb = seg_rows_of(c, q_len);
+    return (rows + rpb - 1) / rpb;
 }
 
 int64_t segs_per_seq_of(const kvattn_config& c, int q_len) {
@@ -141,7 +140,7 @@ int validate_config(const kvattn_config* c) {
         return fail(KVATTN_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
     if (c->max_batch < 1) return fail(KVATTN_ERR_INVALID_ARG, "max_batch must be >= 1");
     if (c->max_q_len < 1 || c->max_q_len > kMaxQLen)
-        return fail(KVATTN_ERR_UNSUPPORTED, "max_q_len must be in 1..64");
+        return fail(KVATTN_ERR_UNSUPPORTED, "max_q_len must be in 1..1024");
     if (c->capacity < 1) return fail(KVATTN_ERR_INVALID_ARG, "capacity must be >= 1");
     if (c->layout != KVATTN_LAYOUT_TOKEN_MAJOR && c->layout != KVATTN_LAYOUT_HEAD_MAJOR)
         return fail(KVATTN_ERR_INVALID_ARG, "unknown layout");

@@ -21,6 +21,7 @@ const void* select_valu_kernel(int dtype, int kv_dtype, int head_dim, int rows, 
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,
                               hipStream_t st);
 bool mfma_supported(int dtype, int head_dim, int rows);
+int mfma_rows_per_block(int rows);  // rows of one segment (whole 16-row tiles, at most 64)
 const void* select_mfma_kernel(int dtype, int head_dim, int rows, int cache_mode);
 constexpr int kMfmaThreads = 256;
 

@@ -114,8 +114,15 @@ PAGED_100K_FP8 = PAGED_100K.replace(name="paged_100k_fp8", seed=8, kv_dtype="fp8
 # as a seeded random tree (8 x GQA 8 = 64 rows per KV head).
 TREE_VERIFY = SPEC_VERIFY.replace(name="tree_verify", seed=9, q_len=8, mask_mode="tree")
 
+# Chunked prefill: a chunk of 512 new tokens per sequence against a 7,680-token cached
+# prefix (GQA 4: 2,048 rows per KV head, 32 blocks of 64 on the matrix cores).
+CHUNKED_PREFILL = Case("chunked_prefill", seed=10, batch=4, num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, dtype="bf16", cache_mode="contiguous", capacity=8192,
+                       q_len=512, seq_lens=(8192,) * 4, value_scale=0.5)
+
 CONFIGS = {c.name: c for c in (TINY, DECODE_7B, SPEC_VERIFY, SINK_WINDOW, PAGED_100K,
-                               DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8, TREE_VERIFY)}
+                               DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8, TREE_VERIFY,
+                               CHUNKED_PREFILL)}
 
 
 def tree_words_from_parents(parents) -> list:
@@ -212,6 +219,25 @@ def make_inputs(case: Case, device: str = "cpu") -> dict:
     out["tree_mask"] = tree_mask.to(device) if tree_mask is not None else None
     out["case"] = case
     return out
+
+
+def small_prefill_variants():
+    """Reduced chunked-prefill cases: 100 new rows x GQA 4 (400 rows per KV head, seven
+    blocks of 64 with a ragged last one) on a contiguous cache, one sequence shorter than
+    its chunk; 80 rows x GQA 4 on a paged cache; 70 rows without GQA at head_dim 64 in
+    f16 (a full block of 64 and a ragged one of 6)."""
+    sv = small_variants()
+    return {
+        "prefill_small": CHUNKED_PREFILL.replace(name="prefill_small", batch=2, num_q_heads=8,
+                                                 num_kv_heads=2, capacity=700, q_len=100,
+                                                 seq_lens=(700, 60), seed=41),
+        "prefill_paged": sv["paged_small"].replace(name="prefill_paged", q_len=80,
+                                                   seq_lens=(1600, 500, 81), seed=42),
+        "prefill_d64": CHUNKED_PREFILL.replace(name="prefill_d64", batch=2, num_q_heads=4,
+                                               num_kv_heads=4, head_dim=64, dtype="f16",
+                                               capacity=600, q_len=70, seq_lens=(600, 333),
+                                               seed=43),
+    }
 
 
 def small_tree_variants():

@@ -45,7 +45,7 @@ def test_config_validation_errors():
     bad = [
         (_cfg(head_dim=96), -2),
         (_cfg(num_q_heads=30, num_kv_heads=8), -1),
-        (_cfg(max_q_len=65), -2),
+        (_cfg(max_q_len=1025), -2),
         (_cfg(max_batch=0), -1),
         (_cfg(capacity=0), -1),
         (_cfg(cache_mode="paged", block_size=12, num_blocks=10, capacity=96), -1),

@@ -92,5 +92,6 @@ def test_tree_argument_errors():
     with pytest.raises(kb.KVAttnError):   # ring caches take the sink/window mask only
         hr.decode_tree(rd["q"], rd["k_cache"], rd["v_cache"], None, rd["seq_lens"], 2, words)
     big = case.replace(q_len=65, num_q_heads=2, num_kv_heads=2)
-    with pytest.raises(kb.KVAttnError):   # 64 new rows at most (one mask word per row)
-        kb.KVAttn.for_case(big)
+    hb = kb.KVAttn.for_case(big)
+    with pytest.raises(kb.KVAttnError):   # 64 draft tokens at most (one mask word per row)
+        hb.plan(65, "tree")

@@ -562,3 +562,16 @@ def test_oracle_sharp_scores_match_sdpa():
     got = oracle.decode(case, q, k, v, None, torch.tensor([T], dtype=torch.int32))[0]
     assert np.isfinite(got).all()
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["spec_verify_small", "sink_window_small", "paged_small"])
+def test_attended_pairs_count_the_oracles_rows(name):
+    """Bench accounting for matrix-core-bound steps: (row, position) pairs row by row."""
+    case = workloads.small_variants()[name].replace(q_len=7)
+    inp = workloads.make_inputs(case.replace(num_q_heads=case.num_kv_heads, head_dim=8))
+    n = 0
+    for b in range(case.batch):
+        for i in range(case.q_len):
+            pos, _ = oracle.attended(case, inp["block_table"], inp["seq_lens"], b, i)
+            n += len(pos)
+    assert accounting.attended_pairs(case, inp["seq_lens"].tolist()) == n * case.num_q_heads
