@@ -212,7 +212,7 @@ def main():
             "mask": case.mask_mode, "n_sink": case.n_sink, "window": case.window,
             "seq_lens_sum": int(sum(sl_host)), "layout": a.layout,
             "n_split": n_split, "split_len": split_len,
-            "kernel": ["valu", "mfma"][kernel], "kv_copies_rotated": copies,
+            "kernel": ["valu", "mfma", "prefill_mfma"][kernel], "kv_copies_rotated": copies,
             "parallelism": "single GPU",
         },
         "roofline": {

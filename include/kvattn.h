@@ -224,7 +224,7 @@ KVATTN_API int kvattn_set_split_len(kvattn_handle* h, int32_t split_len);
  * workgroups launched (one per compute unit for the automatic plan), split_len =
  * the minimum unit length in positions (the exact unit length is placed on the
  * device from seq_lens), and the kernel family (0 = vector-ALU rows, 1 =
- * matrix-core rows). */
+ * matrix-core rows, 2 = chunked-prefill blocks of 256 rows on the matrix cores). */
 KVATTN_API int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
                 int32_t window, int32_t* n_split, int32_t* split_len, int32_t* kernel);
 

@@ -104,10 +104,18 @@ bool use_mfma(const kvattn_config& c, int q_len) {
     return kv_dtype_of(c) == c.dtype && kvattn::mfma_supported(c.dtype, c.head_dim, rows_of(c, q_len));
 }
 
+// Chunked prefill (more than 64 rows per KV head, contiguous or ring cache): the
+// prefill kernel's 256-row blocks.
+bool use_prefill(const kvattn_config& c, int q_len) {
+    return kv_dtype_of(c) == c.dtype &&
+           kvattn::prefill_supported(c.dtype, c.head_dim, rows_of(c, q_len), c.cache_mode);
+}
+
 // Rows of one segment as laid out in the workspace (the kernel instance's row block;
 // the matrix-core kernel pads to whole 16-row tiles, at most 64 rows a block).
 int seg_rows_of(const kvattn_config& c, int q_len) {
     const int rows = rows_of(c, q_len);
+    if (use_prefill(c, q_len)) return kvattn::kPrefillRows;
     if (use_mfma(c, q_len)) return kvattn::mfma_rows_per_block(rows);
     return kvattn::valu_rows_per_block(rows);
 }
@@ -204,13 +212,17 @@ int validate_decode_args(const kvattn_handle* h, int32_t q_len, int32_t mask_mod
 // the device at once (occupancy query).
 int resident_for(const kvattn_config& c, int q_len, int num_cus) {
     const int rows = rows_of(c, q_len);
+    const bool prefill = use_prefill(c, q_len);
     const bool mfma = use_mfma(c, q_len);
-    const void* k = mfma ? kvattn::select_mfma_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
-                         : kvattn::select_valu_kernel(c.dtype, kv_dtype_of(c), c.head_dim, rows,
-                                                      c.cache_mode, q_len > 1);
+    const void* k = prefill ? kvattn::select_prefill_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
+                    : mfma  ? kvattn::select_mfma_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
+                            : kvattn::select_valu_kernel(c.dtype, kv_dtype_of(c), c.head_dim, rows,
+                                                         c.cache_mode, q_len > 1);
+    const int threads = prefill ? kvattn::kPrefillThreads
+                        : mfma  ? kvattn::kMfmaThreads
+                                : kvattn::valu_threads(rows);
     int per_cu = 0;
-    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                  &per_cu, k, mfma ? kvattn::kMfmaThreads : kvattn::valu_threads(rows), 0) != hipSuccess ||
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     return std::min(per_cu * num_cus, kMaxResidentWorkgroups);
@@ -389,7 +401,7 @@ int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_si
     if (rc) return rc;
     if (n_split) *n_split = grid;
     if (split_len) *split_len = chunk;
-    if (kernel) *kernel = use_mfma(h->cfg, q_len) ? 1 : 0;
+    if (kernel) *kernel = use_prefill(h->cfg, q_len) ? 2 : (use_mfma(h->cfg, q_len) ? 1 : 0);
     return KVATTN_OK;
 }
 
@@ -475,7 +487,9 @@ int prepare_decode(kvattn_handle* h, const void* q, const void* k_cache, const v
 int launch_decode(kvattn_handle* h, const kvattn::DecodeParams& p, int grid, int32_t q_len) {
     if (grid == 0) return KVATTN_OK;
     hipError_t e =
-        use_mfma(h->cfg, q_len)
+        use_prefill(h->cfg, q_len)
+            ? kvattn::launch_prefill_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
+        : use_mfma(h->cfg, q_len)
             ? kvattn::launch_decode_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
             : kvattn::launch_decode_valu(p, h->cfg.dtype, kv_dtype_of(h->cfg), h->cfg.head_dim,
                                          grid, h->stream);

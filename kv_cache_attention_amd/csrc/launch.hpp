@@ -25,6 +25,24 @@ int mfma_rows_per_block(int rows);  // rows of one segment (whole 16-row tiles, 
 const void* select_mfma_kernel(int dtype, int head_dim, int rows, int cache_mode);
 constexpr int kMfmaThreads = 256;
 
+// Matrix-core kernel for chunked prefill: more than 64 rows per KV head (f16 / bf16,
+// contiguous and ring caches) in blocks of kPrefillRows rows, one segment each.
+hipError_t launch_prefill_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,
+                               hipStream_t st);
+bool prefill_supported(int dtype, int head_dim, int rows, int cache_mode);
+const void* select_prefill_kernel(int dtype, int head_dim, int rows, int cache_mode);
+#ifndef KVATTN_PF_WAVES
+#define KVATTN_PF_WAVES 8  // waves per workgroup
+#endif
+#ifndef KVATTN_PF_RW
+#define KVATTN_PF_RW 2     // 16-row tiles per wave
+#endif
+#ifndef KVATTN_PF_AHEAD
+#define KVATTN_PF_AHEAD 1  // K/V tiles loaded ahead of the one computed (1 or 2)
+#endif
+constexpr int kPrefillThreads = KVATTN_PF_WAVES * 64;
+constexpr int kPrefillRows = KVATTN_PF_WAVES * KVATTN_PF_RW * 16;
+
 // Test entry: the slots each new row attends, through the kernels' own gather code.
 hipError_t launch_debug_gather(const DecodeParams& p, int max_slots, int32_t* slots_out,
                                int32_t* counts_out, hipStream_t st);

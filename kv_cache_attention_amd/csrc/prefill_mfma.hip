@@ -1,0 +1,339 @@
+// Matrix-core kernel for chunked prefill: hundreds of new query rows per KV head
+// against the cached prefix.  The query tiles against key/value tiles with a
+// running softmax of FlashAttention (nextadmin.net lesson "KV cache and Flash
+// Attention", the tiling trick), shaped for gfx950:
+//
+//  * a workgroup of 8 waves owns a block of 256 rows of one KV head (one segment of
+//    the flat decomposition, work_plan.hpp); each wave owns 32 rows (two 16-row
+//    tiles) and keeps their Q^T operand fragments in registers;
+//  * the workgroup streams the segment's positions in tiles of 32 through three LDS
+//    buffers: while tile t is computed, every thread stores tile t + 1 (loaded into
+//    registers during the previous tile) into its buffer and loads tile t + 2, so a
+//    load has two tiles' time to arrive; each K/V byte is fetched once per 256 rows
+//    (the split-KV kernel fetches it once per 64), one barrier per tile;
+//  * S^T = K . Q^T with K read from LDS in the A-operand layout (rows padded by 16
+//    bytes: the 16 positions one read touches fall on distinct banks), the running
+//    (max, sum) per row, O^T += V^T . P^T with V^T read back with the gfx950
+//    transposed LDS read, as in the split-KV kernel.
+// Contiguous and ring caches, causal and sink/window masks; a segment's pieces and
+// their merge are the split-KV kernel's (split_merge.hpp).
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "mfma_common.hpp"
+#include "split_merge.hpp"
+#include "work_plan.hpp"
+
+namespace kvattn {
+
+constexpr int PF_WAVES = KVATTN_PF_WAVES;
+constexpr int PF_THREADS = kPrefillThreads;
+constexpr int PF_RW = KVATTN_PF_RW;             // 16-row tiles per wave
+constexpr int PF_AHEAD = KVATTN_PF_AHEAD;       // tiles loaded ahead of the one computed
+constexpr int PF_ROWS = kPrefillRows;           // rows per workgroup (one segment)
+
+template <int DT, int D, int CACHE>
+__global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const DecodeParams p) {
+    constexpr float NEG_INF = -__builtin_inff();
+    constexpr int KS = D / 32;             // k-steps of 32 along d (S = K Q^T)
+    constexpr int DT16 = D / 16;           // 16-wide d tiles of the output
+    constexpr int CPR = D * 2 / 16;        // 16-byte chunks per K or V row
+    constexpr int KROW = D * 2 + 16;       // LDS bytes per K row (A-operand reads: no conflict)
+    constexpr int VROW = D * 2 + 32;       // LDS bytes per V row (transposed reads: no conflict)
+    constexpr int TCH = TILE * CPR;        // chunks of one tile's K (and of its V)
+    constexpr int NCH = 2 * TCH / PF_THREADS;  // chunks per thread per tile (K and V)
+    static_assert(2 * TCH % PF_THREADS == 0 && NCH >= 1, "tile chunks per thread");
+
+    constexpr int NB = PF_AHEAD + 1;  // LDS tile buffers
+    __shared__ __attribute__((aligned(16))) char kbuf[NB][TILE * KROW];
+    __shared__ __attribute__((aligned(16))) char vbuf[NB][TILE * VROW];
+    constexpr int MROWS = 64;  // rows the merge takes at a time (bounds its registers)
+    __shared__ MergeSmem<MROWS, PF_THREADS> msm;
+
+    const int wg = blockIdx.x;
+    const int n_wg = gridDim.x;
+    const FlatPlan fp = plan_flat<PF_THREADS>(p, n_wg);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int l = tid % 64;
+    const int lr = l % 16;  // operand row / output column
+    const int lq = l / 16;  // operand k-group / output row group
+    const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k);
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v);
+    const float c = p.scale_log2;
+
+    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
+    const int b = pc.b;
+    const int kvh = pc.seg / p.row_blocks;
+    const int row0 = (pc.seg - kvh * p.row_blocks) * PF_ROWS;
+    const int wrow0 = row0 + wave * PF_RW * 16;  // this wave's first row
+    const int32_t j0 = pc.ja;
+    const int32_t j1 = pc.jb;
+    const int32_t n_tiles = (j1 - j0 + TILE - 1) / TILE;
+
+    // rows' new-token index (padding rows act as the last) and their mask bounds
+    const int32_t P0 = s.T - p.q_len;
+    const bool sink_window = p.mask_mode == MASK_SINK_WINDOW;
+    int32_t hi[PF_RW], lo[PF_RW];
+#pragma unroll
+    for (int qt = 0; qt < PF_RW; ++qt) {
+        const int n = wrow0 + qt * 16 + lr;
+        hi[qt] = P0 + (n < p.rows ? n / p.group : p.q_len - 1);
+        lo[qt] = sink_window ? hi[qt] - p.window + 1 : 0;
+    }
+    const int32_t hi_first = P0 + min(wrow0, p.rows - 1) / p.group;  // smallest row position
+
+    // Q^T operand fragments of the wave's rows (B operand: lane l holds d chunk
+    // ks * 4 + l / 16 of row l % 16)
+    u32x4 qf[PF_RW][KS];
+#pragma unroll
+    for (int qt = 0; qt < PF_RW; ++qt) {
+        const int n = wrow0 + qt * 16 + lr;
+        const bool ok = n < p.rows;
+        const int i = ok ? n / p.group : 0;
+        const int h = kvh * p.group + (ok ? n - i * p.group : 0);
+        const int64_t base = (((int64_t)b * p.q_len + i) * p.num_q_heads + h) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[qt][ks] = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) +
+                                                             base + (ks * 4 + lq) * 8)
+                            : u32x4{0, 0, 0, 0};
+    }
+
+    // A tile's K and V chunks: chunk cc of the tile (K first, then V) is position
+    // cc / CPR (within the kind), 16 bytes cc % CPR of its row.  Positions past the
+    // piece read its last position (in bounds; their scores are masked).
+    u32x4 stA[NCH], stB[NCH];  // staging registers of two tiles, roles alternating
+    auto load_tile = [&](int32_t t, u32x4 (&stage)[NCH]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int cc = tid + k * PF_THREADS;
+            const int kind = cc / TCH;
+            const int rem = cc - kind * TCH;
+            const int32_t j = min(j0 + t * TILE + rem / CPR, j1 - 1);
+            const Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
+            const int64_t off = row_offset(p, L, kvh) + (rem % CPR) * 8;
+            stage[k] = *reinterpret_cast<const u32x4*>((kind ? vp : kp) + off);
+        }
+    };
+    auto store_tile = [&](int buf, const u32x4 (&stage)[NCH]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int cc = tid + k * PF_THREADS;
+            const int kind = cc / TCH;
+            const int rem = cc - kind * TCH;
+            char* dst = kind ? vbuf[buf] + (rem / CPR) * VROW : kbuf[buf] + (rem / CPR) * KROW;
+            *reinterpret_cast<u32x4*>(dst + (rem % CPR) * 16) = stage[k];
+        }
+    };
+
+    f32x4 o[DT16][PF_RW];
+#pragma unroll
+    for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < PF_RW; ++qt) o[dt][qt] = f32x4{0, 0, 0, 0};
+    float m[PF_RW], lsum[PF_RW];
+#pragma unroll
+    for (int qt = 0; qt < PF_RW; ++qt) {
+        m[qt] = NEG_INF;
+        lsum[qt] = 0.0f;
+    }
+
+    if (n_tiles > 0) {
+        load_tile(0, stA);
+        store_tile(0, stA);
+    }
+    if (PF_AHEAD == 2 && n_tiles > 1) load_tile(1, stB);
+    __syncthreads();
+    // one tile ahead: the next tile is loaded into x while this one is computed, then
+    // stored into the other buffer (last read a tile ago).  Two ahead: x holds tile
+    // t + 1 (loaded a tile ago) and is stored first, y receives tile t + 2.
+    auto tile = [&](int32_t t, u32x4 (&x)[NCH], u32x4 (&y)[NCH]) __attribute__((always_inline)) {
+        const int cur = t % NB;
+        if constexpr (PF_AHEAD == 2) {
+            if (t + 1 < n_tiles) store_tile((t + 1) % NB, x);  // its buffer was last read at t - 2
+            if (t + 2 < n_tiles) load_tile(t + 2, y);
+        } else {
+            (void)y;
+            if (t + 1 < n_tiles) load_tile(t + 1, x);
+        }
+        const int32_t tb = j0 + t * TILE;
+        const char* kb = kbuf[cur];
+
+        // S^T = K . Q^T: each K fragment serves both row tiles, each Q fragment both halves
+        f32x4 st[2][PF_RW];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int qt = 0; qt < PF_RW; ++qt) st[tt][qt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(
+                    kb + (tt * 16 + lr) * KROW + (ks * 32 + lq * 8) * 2);
+#pragma unroll
+                for (int qt = 0; qt < PF_RW; ++qt)
+                    st[tt][qt] = mfma16x16x32<DT>(kf, qf[qt][ks], st[tt][qt]);
+            }
+        }
+
+        // mask where it can bite: a partial tile, rows that do not all see the tile's
+        // last position, or the window mask
+        const bool edge = (tb + TILE > j1) || sink_window ||
+                          span_pos(s, min(tb + TILE, j1) - 1) > hi_first;
+        if (edge) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t j = tb + tt * 16 + lq * 4 + e;
+                    const int32_t pos = span_pos(s, min(j, j1 - 1));
+#pragma unroll
+                    for (int qt = 0; qt < PF_RW; ++qt) {
+                        const bool ok = (j < j1) & (pos <= hi[qt]) &
+                                        ((pos < p.n_sink) | (pos >= lo[qt]));
+                        st[tt][qt][e] = ok ? st[tt][qt][e] : NEG_INF;
+                    }
+                }
+            }
+        }
+
+        // online softmax per row (the lane's column lr of each row tile)
+        uint32_t pf[PF_RW][4];
+        bool rescale = false;
+        float alpha[PF_RW];
+#pragma unroll
+        for (int qt = 0; qt < PF_RW; ++qt) {
+            float mt = st[0][qt][0];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mt = fmaxf(mt, st[tt][qt][e]);
+            mt = xmax_16_32(mt);
+            const float m_new = fmaxf(m[qt], mt * c);
+            const float m_use = m_new == NEG_INF ? 0.0f : m_new;
+            alpha[qt] = fast_exp2(m[qt] - m_use);
+            rescale |= m_new != m[qt];
+            m[qt] = m_new;
+            float pw[2][4];
+            float ps = 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pw[tt][e] = fast_exp2(fmaf(st[tt][qt][e], c, -m_use));
+                    ps += pw[tt][e];
+                }
+            lsum[qt] = lsum[qt] * alpha[qt] + ps;
+            pf[qt][0] = pack2<DT>(pw[0][0], pw[0][1]);
+            pf[qt][1] = pack2<DT>(pw[0][2], pw[0][3]);
+            pf[qt][2] = pack2<DT>(pw[1][0], pw[1][1]);
+            pf[qt][3] = pack2<DT>(pw[1][2], pw[1][3]);
+        }
+        if (__any(rescale)) {
+#pragma unroll
+            for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+                for (int qt = 0; qt < PF_RW; ++qt) o[dt][qt] *= alpha[qt];
+        }
+
+        // O^T += V^T . P^T, V^T through the transposed read (lane layout as in the
+        // split-KV kernel: lane j of a 16-lane group gets d = dt * 16 + j at 4 positions)
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef s16x4 __attribute__((address_space(3))) * lds_s16x4;
+        const uint32_t vrow0 =
+            (uint32_t)(size_t)vbuf[cur] + (lq * 4 + lr / 4) * VROW + (lr % 4) * 8;
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) {
+            const uint32_t a0 = vrow0 + dt * 32;
+            const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(size_t)a0);
+            const s16x4 h1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(size_t)(a0 + 16 * VROW));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, h0);
+            const u32x2 w1 = __builtin_bit_cast(u32x2, h1);
+            const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+#pragma unroll
+            for (int qt = 0; qt < PF_RW; ++qt) {
+                const u32x4 pb = {pf[qt][0], pf[qt][1], pf[qt][2], pf[qt][3]};
+                o[dt][qt] = mfma16x16x32<DT>(va, pb, o[dt][qt]);
+            }
+        }
+        if constexpr (PF_AHEAD == 1)
+            if (t + 1 < n_tiles) store_tile((t + 1) % NB, x);
+        __syncthreads();
+    };
+    for (int32_t t = 0; t < n_tiles; t += 2) {
+        tile(t, stB, stA);
+        if (t + 1 < n_tiles) tile(t + 1, stA, stB);
+    }
+
+    // rows out: each wave writes its own rows (final rows, or this piece's partial)
+#pragma unroll
+    for (int qt = 0; qt < PF_RW; ++qt) {
+        const float lt = xsum_16_32(lsum[qt]);
+        const int nb = wave * PF_RW * 16 + qt * 16 + lr;  // row within the segment
+        const bool live = row0 + nb < p.rows;
+        const int64_t rid = live ? row_id_of(p, b, kvh, row0 + nb) : 0;
+        const int64_t part = (pc.slot0 + pc.part) * PF_ROWS + nb;
+        if (live && pc.nparts > 1 && lq == 0) store_partial_ml(p, part, m[qt], lt);
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) {
+            if (!live) continue;
+            const int d = dt * 16 + lq * 4;
+            const f32x4 v = o[dt][qt];
+            if (pc.nparts == 1) {
+                const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+                const uint2 w = {pack2<DT>(v[0] * inv, v[1] * inv), pack2<DT>(v[2] * inv, v[3] * inv)};
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
+            } else {
+                store_partial4(p, part * D + d, float4{v[0], v[1], v[2], v[3]});
+            }
+        }
+    }
+    if (pc.nparts > 1 && arrive(p, pc.unit, pc.nparts)) {
+#pragma unroll 1
+        for (int r0 = 0; r0 < PF_ROWS && row0 + r0 < p.rows; r0 += MROWS) {
+            merge_partials<DT, D, MROWS, PF_THREADS>(p, b, kvh, row0 + r0, pc.unit, pc.slot0,
+                                                     pc.nparts, msm, r0);
+            __syncthreads();  // msm is reused by the next rows
+        }
+    }
+    __syncthreads();  // LDS is reused by the next piece
+    });
+    });
+    zero_empty_sequences<DT, PF_THREADS, D>(p, wg, n_wg);
+}
+
+bool prefill_supported(int dtype, int head_dim, int rows, int cache_mode) {
+    return (dtype == F16 || dtype == BF16) && (head_dim == 64 || head_dim == 128) &&
+           rows > 64 && cache_mode != PAGED;
+}
+
+template <int DT, int D>
+static const void* prefill_kernel_c(int cache_mode) {
+    return cache_mode == RING ? reinterpret_cast<const void*>(&prefill_mfma_kernel<DT, D, RING>)
+                              : reinterpret_cast<const void*>(&prefill_mfma_kernel<DT, D, CONTIGUOUS>);
+}
+
+const void* select_prefill_kernel(int dtype, int head_dim, int rows, int cache_mode) {
+    if (!prefill_supported(dtype, head_dim, rows, cache_mode)) return nullptr;
+    if (dtype == F16)
+        return head_dim == 128 ? prefill_kernel_c<F16, 128>(cache_mode)
+                               : prefill_kernel_c<F16, 64>(cache_mode);
+    return head_dim == 128 ? prefill_kernel_c<BF16, 128>(cache_mode)
+                           : prefill_kernel_c<BF16, 64>(cache_mode);
+}
+
+hipError_t launch_prefill_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,
+                               hipStream_t st) {
+    const void* k = select_prefill_kernel(dtype, head_dim, p.rows, p.cache_mode);
+    if (!k) return hipErrorInvalidValue;
+    DecodeParams pp = p;
+    void* args[] = {&pp};
+    return hipLaunchKernel(k, dim3(grid), dim3(PF_THREADS), args, 0, st);
+}
+
+}  // namespace kvattn

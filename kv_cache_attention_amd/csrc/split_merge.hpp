@@ -100,12 +100,13 @@ struct MergeSmem {
 };
 
 // Merges the nvalid partials of rows row0 .. row0 + NROWS - 1 of KV head kvh
-// (slots slot0 ..) into the output and puts the segment's counter back to zero.
-// Called by every thread of the workgroup that drew the segment's last ticket.
+// (rows roff .. of slots slot0 ..) into the output and puts the segment's counter
+// back to zero.  Called by every thread of the workgroup that drew the segment's
+// last ticket.
 template <int DT, int D, int NROWS, int THREADS>
 __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int kvh, int row0,
                                                int64_t unit, int64_t slot0, int nvalid,
-                                               MergeSmem<NROWS, THREADS>& sm) {
+                                               MergeSmem<NROWS, THREADS>& sm, int roff = 0) {
     static_assert(THREADS % 64 == 0, "whole waves");
     const int tid = threadIdx.x;
     constexpr float NEG_INF = -__builtin_inff();
@@ -121,7 +122,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
     {
         const int r = tid / G, g = tid % G;
         const bool act = r < NROWS && row0 + r < p.rows;
-        const int64_t part0 = act ? slot0 * NR + r : 0;
+        const int64_t part0 = act ? slot0 * NR + roff + r : 0;
         float mx = NEG_INF, ls = 0.0f;
         for (int sp0 = g; sp0 < nvalid; sp0 += 8 * G) {
             float2 v[8];
@@ -176,7 +177,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
         e4[k] = in ? e : 0;
         r[k] = e4[k] / (D / 4);
         live[k] = in && row0 + r[k] < p.rows;
-        part0[k] = live[k] ? slot0 * NR + r[k] : 0;
+        part0[k] = live[k] ? slot0 * NR + roff + r[k] : 0;
         mu[k] = live[k] ? sm.M[r[k]] : 0.0f;
         a[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -235,18 +236,24 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
     if (tid == 0) atomicExch(p.counters + unit, 0);  // ready for the next call
 }
 
-// Called by every thread of the workgroup after it wrote its partial of rows
-// row0 .. row0 + NROWS - 1 of KV head kvh into slot slot0 + (its piece).  Returns
-// after the merge (last workgroup of the segment) or right away (the others).
-template <int DT, int D, int NROWS, int THREADS>
-__device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0, int64_t unit,
-                                 int64_t slot0, int nvalid, MergeSmem<NROWS, THREADS>& sm) {
+// Called by every thread of the workgroup after it wrote its partial into slot
+// slot0 + (its piece) of segment `unit`: takes the segment's ticket once every
+// thread's stores are acknowledged; true for the workgroup that drew the last one.
+__device__ __forceinline__ bool arrive(const DecodeParams& p, int64_t unit, int nvalid) {
     __shared__ int s_last;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
     __syncthreads();                 // ... and every other thread's
     if (threadIdx.x == 0) s_last = atomicAdd(p.counters + unit, 1) == nvalid - 1;
     __syncthreads();
-    if (s_last) merge_partials<DT, D, NROWS, THREADS>(p, b, kvh, row0, unit, slot0, nvalid, sm);
+    return s_last;
+}
+
+// arrive, then (last workgroup of the segment) merge rows row0 .. row0 + NROWS - 1.
+template <int DT, int D, int NROWS, int THREADS>
+__device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0, int64_t unit,
+                                 int64_t slot0, int nvalid, MergeSmem<NROWS, THREADS>& sm) {
+    if (arrive(p, unit, nvalid))
+        merge_partials<DT, D, NROWS, THREADS>(p, b, kvh, row0, unit, slot0, nvalid, sm);
 }
 
 }  // namespace kvattn
