@@ -225,7 +225,8 @@ def small_prefill_variants():
     """Reduced chunked-prefill cases: 100 new rows x GQA 4 (400 rows per KV head, seven
     blocks of 64 with a ragged last one) on a contiguous cache, one sequence shorter than
     its chunk; 80 rows x GQA 4 on a paged cache; 70 rows without GQA at head_dim 64 in
-    f16 (a full block of 64 and a ragged one of 6)."""
+    f16 (a full block of 64 and a ragged one of 6); 100 rows on the StreamingLLM ring
+    with its sink/window mask (the window rolling across the chunk)."""
     sv = small_variants()
     return {
         "prefill_small": CHUNKED_PREFILL.replace(name="prefill_small", batch=2, num_q_heads=8,
@@ -237,6 +238,8 @@ def small_prefill_variants():
                                                num_kv_heads=4, head_dim=64, dtype="f16",
                                                capacity=600, q_len=70, seq_lens=(600, 333),
                                                seed=43),
+        "prefill_ring": sv["sink_window_small"].replace(name="prefill_ring", q_len=100,
+                                                        seed=44),
     }
 
 

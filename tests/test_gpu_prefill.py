@@ -1,7 +1,8 @@
-"""GPU parity of chunked prefill (q_len in the hundreds; rows in blocks of 64 on the
-matrix cores) through the C ABI against the oracle: reduced cases in both layouts with
-never-attended slots poisoned (contiguous and paged caches, a sequence shorter than its
-chunk, head_dim 64), sharp softmax, forced unit lengths (blocks cut into many pieces),
+"""GPU parity of chunked prefill (q_len in the hundreds: the prefill kernel's 256-row
+blocks for contiguous and ring caches, 64-row blocks of the split-KV matrix-core kernel
+for paged ones) through the C ABI against the oracle: reduced cases in both layouts with
+never-attended slots poisoned (contiguous, ring with the sink/window mask, paged, a
+sequence shorter than its chunk, head_dim 64), sharp softmax, forced unit lengths (blocks cut into many pieces),
 and the first rows of a chunk equal to a decode of the shorter prefix."""
 import pytest
 import torch
@@ -32,7 +33,8 @@ def test_prefill_small_workloads_match_oracle(name, layout):
     case = PREFILL[name]
     print(f"prefill case={name} layout={layout}", flush=True)
     h = kb.KVAttn.for_case(case, layout=layout)
-    assert h.plan(case.q_len)[2] == (1 if case.cache_mode == "paged" else 2), "matrix-core kernel"
+    kernel = h.plan(case.q_len, case.mask_mode, case.n_sink, case.window)[2]
+    assert kernel == (1 if case.cache_mode == "paged" else 2), "matrix-core kernel"
     inp, ref = _prep(case)
     out = gh.run(case, gh.to_device(inp), layout=layout, handle=h)
     gh.check(out, ref, case.dtype, f"{name}/{layout}")
