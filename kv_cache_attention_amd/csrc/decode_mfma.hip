@@ -422,7 +422,10 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
 bool mfma_supported(int dtype, int head_dim, int rows) {
     return (dtype == F16 || dtype == BF16) && (head_dim == 64 || head_dim == 128) && rows >= 16;
 }
-int mfma_rows_per_block(int rows) { return rows <= 64 ? (rows + 15) / 16 * 16 : 64; }
+int mfma_rows_per_block(int rows) {
+    constexpr int MAXR = KVATTN_MFMA_MAX_R * 16;
+    return rows <= MAXR ? (rows + 15) / 16 * 16 : MAXR;
+}
 
 template <int DT, int D, int R>
 static const void* mfma_kernel_c(int cache_mode) {
@@ -435,7 +438,7 @@ static const void* mfma_kernel_c(int cache_mode) {
 
 template <int DT, int D>
 static const void* mfma_kernel_r(int rows, int cache_mode) {
-    switch ((rows + 15) / 16) {
+    switch (mfma_rows_per_block(rows) / 16) {
     case 1: return mfma_kernel_c<DT, D, 1>(cache_mode);
     case 2: return mfma_kernel_c<DT, D, 2>(cache_mode);
     case 3: return mfma_kernel_c<DT, D, 3>(cache_mode);

@@ -40,6 +40,12 @@ const void* select_prefill_kernel(int dtype, int head_dim, int rows, int cache_m
 #ifndef KVATTN_PF_AHEAD
 #define KVATTN_PF_AHEAD 1  // K/V tiles loaded ahead of the one computed (1 or 2)
 #endif
+#ifndef KVATTN_MFMA_MAX_R
+#define KVATTN_MFMA_MAX_R 4  // 16-row tiles of a split-KV matrix-core row block (1 .. 4)
+#endif
+#ifndef KVATTN_PF_MIN_ROWS
+#define KVATTN_PF_MIN_ROWS 64  // segments with more rows than this take the prefill kernel
+#endif
 constexpr int kPrefillThreads = KVATTN_PF_WAVES * 64;
 constexpr int kPrefillRows = KVATTN_PF_WAVES * KVATTN_PF_RW * 16;
 

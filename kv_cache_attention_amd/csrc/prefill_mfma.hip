@@ -6,17 +6,18 @@
 //  * a workgroup of 8 waves owns a block of 256 rows of one KV head (one segment of
 //    the flat decomposition, work_plan.hpp); each wave owns 32 rows (two 16-row
 //    tiles) and keeps their Q^T operand fragments in registers;
-//  * the workgroup streams the segment's positions in tiles of 32 through three LDS
-//    buffers: while tile t is computed, every thread stores tile t + 1 (loaded into
-//    registers during the previous tile) into its buffer and loads tile t + 2, so a
-//    load has two tiles' time to arrive; each K/V byte is fetched once per 256 rows
-//    (the split-KV kernel fetches it once per 64), one barrier per tile;
+//  * the workgroup streams the segment's positions in tiles of 32 through two LDS
+//    buffers: while tile t is computed from one, every thread loads tile t + 1 into
+//    registers and stores it into the other after its matrix work, so a load has a
+//    tile's time to arrive (KVATTN_PF_AHEAD=2: three buffers, two tiles' time); each
+//    K/V byte is fetched once per 256 rows (the split-KV kernel fetches it once per
+//    64), one barrier per tile;
 //  * S^T = K . Q^T with K read from LDS in the A-operand layout (rows padded by 16
 //    bytes: the 16 positions one read touches fall on distinct banks), the running
 //    (max, sum) per row, O^T += V^T . P^T with V^T read back with the gfx950
 //    transposed LDS read, as in the split-KV kernel.
-// Contiguous and ring caches, causal and sink/window masks; a segment's pieces and
-// their merge are the split-KV kernel's (split_merge.hpp).
+// Contiguous and ring caches; causal, sink/window and token-tree masks.  A segment's
+// pieces and their merge are the split-KV kernel's (split_merge.hpp).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -72,17 +73,23 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
     const int32_t j1 = pc.jb;
     const int32_t n_tiles = (j1 - j0 + TILE - 1) / TILE;
 
-    // rows' new-token index (padding rows act as the last) and their mask bounds
+    // rows' new-token index (padding rows act as the last) and their mask bounds; a
+    // tree mask lets a row see every position before the new block and new position
+    // P0 + j iff bit j of its word is set
     const int32_t P0 = s.T - p.q_len;
     const bool sink_window = p.mask_mode == MASK_SINK_WINDOW;
-    int32_t hi[PF_RW], lo[PF_RW];
+    const bool tree = p.mask_mode == MASK_TREE;
+    int32_t hi[PF_RW];
+    uint64_t tm[PF_RW];
 #pragma unroll
     for (int qt = 0; qt < PF_RW; ++qt) {
         const int n = wrow0 + qt * 16 + lr;
-        hi[qt] = P0 + (n < p.rows ? n / p.group : p.q_len - 1);
-        lo[qt] = sink_window ? hi[qt] - p.window + 1 : 0;
+        const int i = n < p.rows ? n / p.group : p.q_len - 1;
+        hi[qt] = tree ? s.T - 1 : P0 + i;
+        tm[qt] = tree ? p.tree_mask[(int64_t)b * p.q_len + i] : ~0ull;
     }
-    const int32_t hi_first = P0 + min(wrow0, p.rows - 1) / p.group;  // smallest row position
+    // smallest position a row of this wave sits at (a tree's rows all see up to P0 - 1)
+    const int32_t hi_first = tree ? P0 - 1 : P0 + min(wrow0, p.rows - 1) / p.group;
 
     // Q^T operand fragments of the wave's rows (B operand: lane l holds d chunk
     // ks * 4 + l / 16 of row l % 16)
@@ -160,7 +167,6 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
         }
         const int32_t tb = j0 + t * TILE;
         const char* kb = kbuf[cur];
-
         // S^T = K . Q^T: each K fragment serves both row tiles, each Q fragment both halves
         f32x4 st[2][PF_RW];
 #pragma unroll
@@ -190,10 +196,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
                 for (int e = 0; e < 4; ++e) {
                     const int32_t j = tb + tt * 16 + lq * 4 + e;
                     const int32_t pos = span_pos(s, min(j, j1 - 1));
+                    const int32_t rel = pos - P0;
+                    const uint64_t bit = rel >= 0 ? 1ull << (rel & 63) : 0ull;
 #pragma unroll
                     for (int qt = 0; qt < PF_RW; ++qt) {
                         const bool ok = (j < j1) & (pos <= hi[qt]) &
-                                        ((pos < p.n_sink) | (pos >= lo[qt]));
+                                        (!sink_window | (pos < p.n_sink) |
+                                         (pos > hi[qt] - p.window)) &
+                                        ((rel < 0) | ((tm[qt] & bit) != 0));
                         st[tt][qt][e] = ok ? st[tt][qt][e] : NEG_INF;
                     }
                 }
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
 
 bool prefill_supported(int dtype, int head_dim, int rows, int cache_mode) {
     return (dtype == F16 || dtype == BF16) && (head_dim == 64 || head_dim == 128) &&
-           rows > 64 && cache_mode != PAGED;
+           rows > KVATTN_PF_MIN_ROWS && cache_mode != PAGED;
 }
 
 template <int DT, int D>

@@ -115,7 +115,7 @@ PAGED_100K_FP8 = PAGED_100K.replace(name="paged_100k_fp8", seed=8, kv_dtype="fp8
 TREE_VERIFY = SPEC_VERIFY.replace(name="tree_verify", seed=9, q_len=8, mask_mode="tree")
 
 # Chunked prefill: a chunk of 512 new tokens per sequence against a 7,680-token cached
-# prefix (GQA 4: 2,048 rows per KV head, 32 blocks of 64 on the matrix cores).
+# prefix (GQA 4: 2,048 rows per KV head, eight 256-row blocks of the prefill kernel).
 CHUNKED_PREFILL = Case("chunked_prefill", seed=10, batch=4, num_q_heads=32, num_kv_heads=8,
                        head_dim=128, dtype="bf16", cache_mode="contiguous", capacity=8192,
                        q_len=512, seq_lens=(8192,) * 4, value_scale=0.5)
@@ -245,8 +245,11 @@ def small_prefill_variants():
 
 def small_tree_variants():
     """Reduced token-tree verification cases: 5 and 8 draft tokens with GQA 8 (40 and
-    64 rows per KV head: matrix-core kernel), 6 tokens without GQA and 7 tokens on a
-    paged cache with GQA 4 (vector-ALU kernel), and sequences shorter than their tree."""
+    64 rows per KV head) and 7 on a paged cache with GQA 4 (28 rows; all three on the
+    split-KV matrix-core kernel), 6 tokens without GQA (vector-ALU kernel), wide trees
+    of 40 and 64 tokens with GQA 8 (320 and 512 rows: the prefill kernel's 256-row
+    blocks, one of them ragged) and of 30 tokens on a paged cache (120 rows: two
+    64-row blocks of the split-KV kernel), and sequences shorter than their tree."""
     sv = small_variants()
     base = sv["spec_verify_small"].replace(mask_mode="tree")
     return {
@@ -257,6 +260,10 @@ def small_tree_variants():
                                                    q_len=6, seq_len_range=(1, 1200), seed=34),
         "tree_paged": sv["paged_small"].replace(name="tree_paged", mask_mode="tree", q_len=7,
                                                 seed=35),
+        "tree_wide": base.replace(name="tree_wide", q_len=40, seed=36),
+        "tree_q64": base.replace(name="tree_q64", q_len=64, seq_lens=(1000, 64, 40), seed=37),
+        "tree_wide_paged": sv["paged_small"].replace(name="tree_wide_paged", mask_mode="tree",
+                                                     q_len=30, seed=38),
     }
 
 

@@ -1,8 +1,9 @@
 """GPU parity of token-tree verification (kvattn_decode_tree) through the C ABI: the
-reduced tree cases (matrix-core and vector-ALU kernels, contiguous and paged caches,
-sequences shorter than their tree) against the oracle in both layouts with never-
-attended slots poisoned, sharp softmax, a chain tree bit-equal to the causal decode,
-the tree gather bit-exact against the oracle's enumerator, and the argument checks."""
+reduced tree cases (split-KV matrix-core, vector-ALU and prefill kernels, contiguous and
+paged caches, sequences shorter than their tree) against the oracle in both layouts
+with never-attended slots poisoned, sharp softmax, a chain tree bit-equal to the causal
+decode, the tree gather bit-exact against the oracle's enumerator, the kernel each case
+takes, and the argument checks."""
 import numpy as np
 import pytest
 import torch
@@ -46,7 +47,20 @@ def test_tree_sharp_softmax_matches_oracle(name):
     gh.check(out, ref, case.dtype, f"{name}/sharp")
 
 
-@pytest.mark.parametrize("name", ["tree_small", "tree_valu", "tree_paged"])
+# kernel codes of kvattn_plan: 0 vector ALU, 1 split-KV matrix core, 2 prefill
+KERNELS = {"tree_small": 1, "tree_small_q8": 1, "tree_short": 1, "tree_valu": 0,
+           "tree_paged": 1, "tree_wide": 2, "tree_q64": 2, "tree_wide_paged": 1}
+
+
+@pytest.mark.parametrize("name", list(TREES))
+def test_tree_cases_take_the_expected_kernel(name):
+    case = TREES[name]
+    h = kb.KVAttn.for_case(case)
+    assert h.plan(case.q_len, "tree")[2] == KERNELS[name]
+
+
+@pytest.mark.parametrize("name", ["tree_small", "tree_valu", "tree_paged", "tree_wide",
+                                  "tree_wide_paged"])
 def test_chain_tree_equals_causal_decode_bit_for_bit(name):
     case = TREES[name]
     print(f"tree case={name} chain", flush=True)
