@@ -38,7 +38,7 @@ const void* select_prefill_kernel(int dtype, int head_dim, int rows, int cache_m
 #define KVATTN_PF_RW 2     // 16-row tiles per wave
 #endif
 #ifndef KVATTN_PF_AHEAD
-#define KVATTN_PF_AHEAD 1  // K/V tiles loaded ahead of the one computed (1 or 2)
+#define KVATTN_PF_AHEAD 2  // K/V tiles in flight in registers (1 or 2)
 #endif
 #ifndef KVATTN_MFMA_MAX_R
 #define KVATTN_MFMA_MAX_R 4  // 16-row tiles of a split-KV matrix-core row block (1 .. 4)

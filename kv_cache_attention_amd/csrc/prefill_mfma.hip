@@ -7,11 +7,11 @@
 //    the flat decomposition, work_plan.hpp); each wave owns 32 rows (two 16-row
 //    tiles) and keeps their Q^T operand fragments in registers;
 //  * the workgroup streams the segment's positions in tiles of 32 through two LDS
-//    buffers: while tile t is computed from one, every thread loads tile t + 1 into
-//    registers and stores it into the other after its matrix work, so a load has a
-//    tile's time to arrive (KVATTN_PF_AHEAD=2: three buffers, two tiles' time); each
-//    K/V byte is fetched once per 256 rows (the split-KV kernel fetches it once per
-//    64), one barrier per tile;
+//    buffers: while tile t is computed from one, every thread holds its share of the
+//    next KVATTN_PF_AHEAD tiles in registers (loads in flight) and, after its matrix
+//    work, stores tile t + 1 into the other buffer; one barrier per tile.  Each K/V
+//    byte is fetched once per row block (the split-KV kernel fetches it once per 64
+//    rows);
 //  * S^T = K . Q^T with K read from LDS in the A-operand layout (rows padded by 16
 //    bytes: the 16 positions one read touches fall on distinct banks), the running
 //    (max, sum) per row, O^T += V^T . P^T with V^T read back with the gfx950
@@ -29,7 +29,10 @@ namespace kvattn {
 constexpr int PF_WAVES = KVATTN_PF_WAVES;
 constexpr int PF_THREADS = kPrefillThreads;
 constexpr int PF_RW = KVATTN_PF_RW;             // 16-row tiles per wave
-constexpr int PF_AHEAD = KVATTN_PF_AHEAD;       // tiles loaded ahead of the one computed
+constexpr int PF_AHEAD = KVATTN_PF_AHEAD;       // tiles in flight in registers (1 or 2)
+// Deeper rings are not offered: a four-tile ring (four waves of 16 rows) faulted once on
+// a ring-cache case, and the cause was not established.
+static_assert(PF_AHEAD == 1 || PF_AHEAD == 2, "prefetch depth");
 constexpr int PF_ROWS = kPrefillRows;           // rows per workgroup (one segment)
 
 template <int DT, int D, int CACHE>
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
     constexpr int NCH = 2 * TCH / PF_THREADS;  // chunks per thread per tile (K and V)
     static_assert(2 * TCH % PF_THREADS == 0 && NCH >= 1, "tile chunks per thread");
 
-    constexpr int NB = PF_AHEAD + 1;  // LDS tile buffers
+    constexpr int NB = 2;  // LDS tile buffers
     __shared__ __attribute__((aligned(16))) char kbuf[NB][TILE * KROW];
     __shared__ __attribute__((aligned(16))) char vbuf[NB][TILE * VROW];
     constexpr int MROWS = 64;  // rows the merge takes at a time (bounds its registers)
@@ -110,8 +113,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
 
     // A tile's K and V chunks: chunk cc of the tile (K first, then V) is position
     // cc / CPR (within the kind), 16 bytes cc % CPR of its row.  Positions past the
-    // piece read its last position (in bounds; their scores are masked).
-    u32x4 stA[NCH], stB[NCH];  // staging registers of two tiles, roles alternating
+    // piece read its last position (in bounds; their scores are masked), so loads of
+    // tiles past the last one are harmless and need no branch.
+    u32x4 stg[PF_AHEAD][NCH];  // staging registers: tile t sits in slot t % PF_AHEAD
     auto load_tile = [&](int32_t t, u32x4 (&stage)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
@@ -147,24 +151,20 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
         lsum[qt] = 0.0f;
     }
 
+    // Tiles 0 .. PF_AHEAD - 1 go in flight, tile 0 into LDS.  Step t then loads tile
+    // t + PF_AHEAD into the slot tile t left (stored a step ago), computes tile t from
+    // its buffer, stores tile t + 1 (loaded PF_AHEAD - 1 steps ago) into the other
+    // buffer (last read in step t - 1) and meets the others at the barrier.
     if (n_tiles > 0) {
-        load_tile(0, stA);
-        store_tile(0, stA);
+#pragma unroll
+        for (int a = 0; a < PF_AHEAD; ++a) load_tile(a, stg[a]);
+        store_tile(0, stg[0]);
     }
-    if (PF_AHEAD == 2 && n_tiles > 1) load_tile(1, stB);
     __syncthreads();
-    // one tile ahead: the next tile is loaded into x while this one is computed, then
-    // stored into the other buffer (last read a tile ago).  Two ahead: x holds tile
-    // t + 1 (loaded a tile ago) and is stored first, y receives tile t + 2.
-    auto tile = [&](int32_t t, u32x4 (&x)[NCH], u32x4 (&y)[NCH]) __attribute__((always_inline)) {
+    auto tile = [&](int32_t t, u32x4 (&mine)[NCH], const u32x4 (&next)[NCH])
+                    __attribute__((always_inline)) {
         const int cur = t % NB;
-        if constexpr (PF_AHEAD == 2) {
-            if (t + 1 < n_tiles) store_tile((t + 1) % NB, x);  // its buffer was last read at t - 2
-            if (t + 2 < n_tiles) load_tile(t + 2, y);
-        } else {
-            (void)y;
-            if (t + 1 < n_tiles) load_tile(t + 1, x);
-        }
+        load_tile(t + PF_AHEAD, mine);
         const int32_t tb = j0 + t * TILE;
         const char* kb = kbuf[cur];
         // S^T = K . Q^T: each K fragment serves both row tiles, each Q fragment both halves
@@ -271,13 +271,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
                 o[dt][qt] = mfma16x16x32<DT>(va, pb, o[dt][qt]);
             }
         }
-        if constexpr (PF_AHEAD == 1)
-            if (t + 1 < n_tiles) store_tile((t + 1) % NB, x);
+        if (t + 1 < n_tiles) store_tile((t + 1) % NB, next);
         __syncthreads();
     };
-    for (int32_t t = 0; t < n_tiles; t += 2) {
-        tile(t, stB, stA);
-        if (t + 1 < n_tiles) tile(t + 1, stA, stB);
+    // unrolled by two so every slot index is a constant (PF_AHEAD 1: both steps use slot 0)
+    for (int32_t t = 0; t < n_tiles;) {
+        tile(t, stg[0], stg[1 % PF_AHEAD]);
+        if (++t >= n_tiles) break;
+        tile(t, stg[1 % PF_AHEAD], stg[0]);
+        ++t;
     }
 
     // rows out: each wave writes its own rows (final rows, or this piece's partial)
