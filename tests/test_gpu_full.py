@@ -1,7 +1,8 @@
 """GPU parity at the workloads' full sizes (the five, the 8-bit-cache versions of
-three of them, and token-tree verification), in the launch configuration the benchmark times (automatic plan,
-head-major caches): sampled output rows against the oracle computed row by row, plus
-NaN poison in never-attended slots and the sharp (q x 8) variant of each."""
+three of them, token-tree verification and chunked prefill), in the launch configuration
+the benchmark times (automatic plan, head-major caches): sampled output rows against
+the oracle computed row by row, plus NaN poison in never-attended slots and the sharp
+(q x 8) variant of each."""
 import numpy as np
 import pytest
 import torch
