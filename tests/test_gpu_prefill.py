@@ -3,7 +3,8 @@ blocks for contiguous and ring caches, 64-row blocks of the split-KV matrix-core
 for paged ones) through the C ABI against the oracle: reduced cases in both layouts with
 never-attended slots poisoned (contiguous, ring with the sink/window mask, paged, a
 sequence shorter than its chunk, head_dim 64), sharp softmax, forced unit lengths (blocks cut into many pieces),
-and the first rows of a chunk equal to a decode of the shorter prefix."""
+the first rows of a chunk equal to a decode of the shorter prefix, and chunks of the
+largest q_len (1024) on each kernel, with sequences shorter than their chunk."""
 import pytest
 import torch
 
@@ -15,6 +16,21 @@ from tests import gpu_helpers as gh
 pytestmark = pytest.mark.gpu
 
 PREFILL = workloads.small_prefill_variants()
+
+# q_len 1024 (the most a handle accepts): 4,096 rows per KV head on the prefill kernel
+# (16 blocks) and on the split-KV kernel (paged, 64 blocks), 1,024 on the vector-ALU
+# kernel (f32); one sequence in each is shorter than its chunk.
+_SV = workloads.small_variants()
+MAX_Q = {
+    "prefill_max": (workloads.CHUNKED_PREFILL.replace(
+        name="prefill_max", batch=2, num_q_heads=8, num_kv_heads=2, capacity=1536,
+        q_len=1024, seq_lens=(1536, 1000), seed=45), 2),
+    "prefill_max_paged": (_SV["paged_small"].replace(
+        name="prefill_max_paged", q_len=1024, seq_lens=(1600, 1377, 33), seed=46), 1),
+    "prefill_max_f32": (_SV["decode_7b_small"].replace(
+        name="prefill_max_f32", dtype="f32", batch=2, capacity=1200, seq_len_range=None,
+        seq_lens=(1200, 1100), q_len=1024, seed=47), 0),
+}
 
 
 def _prep(case, scale_q=1.0):
@@ -75,3 +91,15 @@ def test_first_chunk_rows_equal_a_decode_of_the_prefix():
                         ds["seq_lens"].cpu())
     gh.check(part, ref, case.dtype, "prefix verify")
     gh.check(full[:, :20], ref, case.dtype, "chunk head")
+
+
+@pytest.mark.parametrize("name", list(MAX_Q))
+@pytest.mark.parametrize("layout", ["token_major", "head_major"])
+def test_largest_chunk_matches_oracle(name, layout):
+    case, kernel = MAX_Q[name]
+    print(f"prefill case={name} layout={layout}", flush=True)
+    h = kb.KVAttn.for_case(case, layout=layout)
+    assert h.plan(case.q_len)[2] == kernel
+    inp, ref = _prep(case)
+    out = gh.run(case, gh.to_device(inp), layout=layout, handle=h)
+    gh.check(out, ref, case.dtype, f"{name}/{layout}")
