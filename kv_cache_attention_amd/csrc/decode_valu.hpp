@@ -475,9 +475,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
                 float mt = sc[r][0];
 #pragma unroll
                 for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[r][u]);
-                const float m_new = fmaxf(m[r], mt * cp);  // cp > 0: max commutes with the scale
+                const float m_top = fmaxf(m[r], mt * cp);  // cp > 0: max commutes with the scale
+                const float m_new = m_top > m[r] + RESCALE_SLACK ? m_top : m[r];  // lazy
                 const float m_use = m_new == NEG_INF ? 0.0f : m_new;
-                if (__any(m_new != m[r])) {  // rescale only when some lane's max moved
+                if (__any(m_new != m[r])) {  // rescale only when some lane's reference moved
                     const float alpha = fast_exp2(m[r] - m_use);  // 0 while nothing was seen
                     l[r] *= alpha;
 #pragma unroll

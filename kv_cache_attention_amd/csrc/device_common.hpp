@@ -45,6 +45,13 @@ struct DecodeParams {
     float scale_log2;     // softmax scale * log2(e): scores are kept in the exp2 domain
 };
 
+// Lazy rescaling of the running softmax: a row's reference maximum moves only when a
+// score exceeds it by more than 2^RESCALE_SLACK (log2 units).  Until then the weights
+// exp2(s - m) stay below 2^RESCALE_SLACK, well inside the range of the 16-bit types
+// they may be packed to, and O and the row sum keep one common reference, so the
+// normalised result is the same quantity; the accumulators are rescaled far less often.
+constexpr float RESCALE_SLACK = 8.0f;
+
 // The attended positions of one sequence, over all q_len new rows, are the union
 // [0, sink) + [tail, T): sink positions (attention sinks) and one trailing run.
 // Work is indexed by j in [0, count): j < sink -> position j, else tail + (j - sink).

@@ -222,7 +222,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mt = fmaxf(mt, st[tt][qt][e]);
             mt = xmax_16_32(mt);
-            const float m_new = fmaxf(m[qt], mt * c);
+            const float m_top = fmaxf(m[qt], mt * c);
+            const float m_new = m_top > m[qt] + RESCALE_SLACK ? m_top : m[qt];  // lazy
             const float m_use = m_new == NEG_INF ? 0.0f : m_new;
             alpha[qt] = fast_exp2(m[qt] - m_use);
             rescale |= m_new != m[qt];
