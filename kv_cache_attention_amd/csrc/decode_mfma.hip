@@ -279,43 +279,56 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         // online softmax per row (row = lane column lr of each row tile); scores stay
         // raw, the scale enters through the exp2 argument
         uint32_t pf[R][4];
-        bool rescale = false;
-        float alpha[R];
+        // The weights are taken against the current reference at once, beside the
+        // tile's maximum; only when some row's reference has to move (lazy rescaling:
+        // rare after a piece's first tile) are they taken again against the new one.
+        float pw[R][2][4], m_top[R];
+        bool move = false;
 #pragma unroll
         for (int qt = 0; qt < R; ++qt) {
+            const float m_use = m[qt] == NEG_INF ? 0.0f : m[qt];
             float mt = st[0][qt][0];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mt = fmaxf(mt, st[tt][qt][e]);
+                for (int e = 0; e < 4; ++e) {
+                    pw[qt][tt][e] = fast_exp2(fmaf(st[tt][qt][e], c, -m_use));
+                    mt = fmaxf(mt, st[tt][qt][e]);
+                }
             mt = xmax_16_32(mt);
-            const float m_top = fmaxf(m[qt], mt * c);
-            const float m_new = m_top > m[qt] + RESCALE_SLACK ? m_top : m[qt];  // lazy
-            const float m_use = m_new == NEG_INF ? 0.0f : m_new;
-            alpha[qt] = fast_exp2(m[qt] - m_use);
-            rescale |= m_new != m[qt];
-            m[qt] = m_new;
-            float pw[2][4];
+            m_top[qt] = fmaxf(m[qt], mt * c);
+            move |= m_top[qt] > m[qt] + RESCALE_SLACK;
+        }
+        if (__any(move)) {
+#pragma unroll
+            for (int qt = 0; qt < R; ++qt) {
+                const float m_new = m_top[qt] > m[qt] + RESCALE_SLACK ? m_top[qt] : m[qt];
+                const float m_use = m_new == NEG_INF ? 0.0f : m_new;
+                const float alpha = fast_exp2(m[qt] - m_use);
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pw[qt][tt][e] = fast_exp2(fmaf(st[tt][qt][e], c, -m_use));
+                lsum[qt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT16; ++dt) o[dt][qt] *= alpha;
+                m[qt] = m_new;
+            }
+        }
+        // P^T operand: k = 8*lq + e -> positions 4*lq+e (first half), 16+4*lq+e (second)
+#pragma unroll
+        for (int qt = 0; qt < R; ++qt) {
             float ps = 0.0f;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pw[tt][e] = fast_exp2(fmaf(st[tt][qt][e], c, -m_use));
-                    ps += pw[tt][e];
-                }
-            lsum[qt] = lsum[qt] * alpha[qt] + ps;
-            // P^T operand: k = 8*lq + e -> positions 4*lq+e (first half), 16+4*lq+e (second)
-            pf[qt][0] = pack2<DT>(pw[0][0], pw[0][1]);
-            pf[qt][1] = pack2<DT>(pw[0][2], pw[0][3]);
-            pf[qt][2] = pack2<DT>(pw[1][0], pw[1][1]);
-            pf[qt][3] = pack2<DT>(pw[1][2], pw[1][3]);
-        }
-        if (__any(rescale)) {
-#pragma unroll
-            for (int dt = 0; dt < DT16; ++dt)
-#pragma unroll
-                for (int qt = 0; qt < R; ++qt) o[dt][qt] *= alpha[qt];
+                for (int e = 0; e < 4; ++e) ps += pw[qt][tt][e];
+            lsum[qt] += ps;
+            pf[qt][0] = pack2<DT>(pw[qt][0][0], pw[qt][0][1]);
+            pf[qt][1] = pack2<DT>(pw[qt][0][2], pw[qt][0][3]);
+            pf[qt][2] = pack2<DT>(pw[qt][1][0], pw[qt][1][1]);
+            pf[qt][3] = pack2<DT>(pw[qt][1][2], pw[qt][1][3]);
         }
 
         // O^T += V^T . P^T.  V^T comes back from LDS with the gfx950 transposed read
