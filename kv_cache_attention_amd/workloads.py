@@ -18,9 +18,14 @@ Workload shapes follow the decode settings the source pages discuss:
     (lesson, "PagedAttention - the KV cache as virtual memory").
 
 Draw order (fixed, so a seed names one input set): integer structure first
-(sequence lengths, block permutation), then Q, K, V as float32 standard
-normals, then the value scale (and the optional boost of K at position 0),
-then the cast to the storage dtype.  An 8-bit KV cache (kv_dtype "fp8", OCP
+(sequence lengths, block permutation, token trees) from torch's CPU generator
+seeded with the case's seed; then Q, K, V as float32 standard normals; then the
+value scale (and the optional boost of K at position 0); then the cast to the
+storage dtype.  The normals of tensor n (0 = Q, 1 = K, 2 = V) are drawn in
+chunks of 2^22 consecutive elements, chunk c from its own CPU generator seeded
+with (seed << 16) | (n << 14) | c (a 32-bit seed: torch's CPU generator keeps
+only the low 32 bits), so the values are the same on every machine and a
+gigabyte cache is drawn by several host threads at once.  An 8-bit KV cache (kv_dtype "fp8", OCP
 E4M3) casts K and V per KV head: scale = max |x| / 448 over that head's slots
 (the largest finite E4M3 magnitude), code = round-to-nearest-even(x / scale);
 the scales (float32 [Hkv]) travel with the inputs as k_scale, v_scale.
@@ -34,7 +39,9 @@ Layouts (row-major, head_dim innermost):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
 from dataclasses import dataclass
 from typing import Optional, Tuple
 
@@ -148,16 +155,50 @@ def cache_shape(case: Case) -> Tuple[int, ...]:
     return (case.batch, case.capacity, case.num_kv_heads, case.head_dim)
 
 
-def make_inputs(case: Case, device: str = "cpu") -> dict:
-    """Draw one input set for `case`.
+CHUNK = 1 << 22  # elements per generator stream
 
-    device="cpu" draws with torch's CPU generator (identical on every machine).
-    device="cuda" draws the same distributions with torch's device generator
-    seeded the same way (a different stream of values, made where the data
-    will live, which keeps multi-GiB caches fast to build).  The integer
-    structure is always drawn on the CPU generator so it is the same either way.
-    Returns a dict of tensors on `device` plus "case".
-    """
+
+def _chunk_seed(seed: int, tensor: int, chunk: int) -> int:
+    assert 0 <= seed < (1 << 16) and 0 <= tensor < 4 and 0 <= chunk < (1 << 14)
+    return (seed << 16) | (tensor << 14) | chunk
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _normals(shape, seed: int, tensor: int, pool) -> torch.Tensor:
+    """float32 standard normals of `shape`: chunk c of the flat tensor from the CPU
+    generator seeded with _chunk_seed(seed, tensor, c)."""
+    n = int(np.prod(shape))
+    x = torch.empty(n, dtype=torch.float32)
+
+    def fill(c):
+        g = torch.Generator("cpu").manual_seed(_chunk_seed(seed, tensor, c))
+        x[c * CHUNK:min(n, (c + 1) * CHUNK)].normal_(generator=g)
+
+    list(pool.map(fill, range((n + CHUNK - 1) // CHUNK)))
+    return x.view(shape)
+
+
+def _cast(x: torch.Tensor, dt: torch.dtype, pool) -> torch.Tensor:
+    """x.to(dt), chunk by chunk on the worker threads (round to nearest even)."""
+    if dt == torch.float32:
+        return x
+    flat = x.reshape(-1)
+    out = torch.empty(flat.shape, dtype=dt)
+
+    def cast(c):
+        sl = slice(c * CHUNK, min(flat.numel(), (c + 1) * CHUNK))
+        out[sl] = flat[sl].to(dt)
+
+    list(pool.map(cast, range((flat.numel() + CHUNK - 1) // CHUNK)))
+    return out.view(x.shape)
+
+
+def make_inputs(case: Case, device: str = "cpu") -> dict:
+    """Draw one input set for `case` on the host (the same values on every machine),
+    then move it to `device`.  Returns a dict of tensors plus "case"."""
     g_cpu = torch.Generator("cpu").manual_seed(case.seed)
 
     # 1. integer structure
@@ -181,39 +222,41 @@ def make_inputs(case: Case, device: str = "cpu") -> dict:
         tree_mask = torch.tensor(np.array(words, dtype=np.uint64).view(np.int64))
 
     # 2. values (float32 standard normals)
-    if device == "cpu":
-        g = g_cpu
-    else:
-        g = torch.Generator(device).manual_seed(case.seed)
     qshape = (case.batch, case.q_len, case.num_q_heads, case.head_dim)
     dt = DTYPES[case.dtype]
     kvdt = case.kv_dtype or case.dtype
     out = {"k_scale": None, "v_scale": None}
-    for name, shape in (("q", qshape), ("k_cache", cache_shape(case)), ("v_cache", cache_shape(case))):
-        x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
-        # 3. scale
-        if case.value_scale != 1.0:
-            x.mul_(case.value_scale)
-        if name == "k_cache" and case.k0_boost != 1.0:
-            # Logical position 0 of each sequence.  Contiguous and ring caches
-            # keep position 0 in the sequence's first slot (sink tokens are
-            # never evicted); a paged cache keeps it at offset 0 of the block
-            # the first page-table entry names.
-            if case.cache_mode == "paged":
-                for b in range(case.batch):
-                    x[int(block_table[b, 0]), 0].mul_(case.k0_boost)
+    with cf.ThreadPoolExecutor(_workers()) as pool:
+        for n, (name, shape) in enumerate((("q", qshape), ("k_cache", cache_shape(case)),
+                                           ("v_cache", cache_shape(case)))):
+            x = _normals(shape, case.seed, n, pool)
+            # 3. scale
+            if case.value_scale != 1.0:
+                x.mul_(case.value_scale)
+            if name == "k_cache" and case.k0_boost != 1.0:
+                # Logical position 0 of each sequence.  Contiguous and ring caches
+                # keep position 0 in the sequence's first slot (sink tokens are
+                # never evicted); a paged cache keeps it at offset 0 of the block
+                # the first page-table entry names.
+                if case.cache_mode == "paged":
+                    for b in range(case.batch):
+                        x[int(block_table[b, 0]), 0].mul_(case.k0_boost)
+                else:
+                    x[:, 0].mul_(case.k0_boost)
+            # 4. cast
+            if name != "q" and kvdt == "fp8":
+                # per KV head (dim 2 of every cache layout): scale = amax / 448
+                amax = x.abs().amax(dim=tuple(d for d in range(x.dim()) if d != 2))
+                sc = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).to(torch.float32)
+                x.div_(sc.view(1, 1, -1, 1))
+                out[name] = _cast(x, torch.float8_e4m3fn, pool)
+                out["k_scale" if name == "k_cache" else "v_scale"] = sc
             else:
-                x[:, 0].mul_(case.k0_boost)
-        # 4. cast
-        if name != "q" and kvdt == "fp8":
-            # per KV head (dim 2 of every cache layout): scale = amax / 448
-            amax = x.abs().amax(dim=tuple(d for d in range(x.dim()) if d != 2))
-            sc = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).to(torch.float32)
-            out[name] = (x / sc.view(1, 1, -1, 1)).to(torch.float8_e4m3fn)
-            out["k_scale" if name == "k_cache" else "v_scale"] = sc
-        else:
-            out[name] = x.to(dt) if dt != torch.float32 else x
-        del x
+                out[name] = _cast(x, dt, pool)
+            del x
+    for k in ("q", "k_cache", "v_cache", "k_scale", "v_scale"):
+        if out[k] is not None:
+            out[k] = out[k].to(device)
     out["seq_lens"] = seq_lens.to(device)
     out["block_table"] = block_table.to(device) if block_table is not None else None
     out["tree_mask"] = tree_mask.to(device) if tree_mask is not None else None

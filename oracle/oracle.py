@@ -268,6 +268,58 @@ def decode_np(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0
     return out
 
 
+def decode_matmul_np(pr, q, k_cache, v_cache, block_table, seq_lens, scale: float = 0.0,
+                     k_scale=None, v_scale=None, tree_mask=None) -> np.ndarray:
+    """float64 [batch, q_len, Hq, D]: softmax(Q K^T / sqrt(d)) V written in matrix form
+    (StreamingLLM article, "The softmax problem"), one (sequence, KV head) at a time:
+    the scores of all q_len x group query rows against the sequence's attended
+    positions as one float64 matrix product, the explicit boolean mask of each new row
+    (-inf where it does not attend), a row-wise softmax, and one more product with V.
+    Same definition as decode_np; the products are library matmuls, which makes the
+    hundreds of rows of a prefill chunk affordable.  A row that attends nothing is 0."""
+    D, Hq, Hkv = pr.head_dim, pr.num_q_heads, pr.num_kv_heads
+    g = Hq // Hkv
+    ql = pr.q_len
+    sc = scale if scale != 0.0 else 1.0 / math.sqrt(D)
+    ks = np.ones(Hkv) if k_scale is None else to_f64(k_scale.float())
+    vs = np.ones(Hkv) if v_scale is None else to_f64(v_scale.float())
+    kflat = _cpu(k_cache).reshape(-1, Hkv, D)
+    vflat = _cpu(v_cache).reshape(-1, Hkv, D)
+    q64 = to_f64(q)
+    sl = np.asarray(seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens)
+    words = None if tree_mask is None else tree_words(tree_mask)
+    out = np.zeros((pr.batch, ql, Hq, D))
+    for b in range(pr.batch):
+        T = int(sl[b])
+        rows = [attended_positions_np(pr.mask_mode, T, ql, i, pr.n_sink, pr.window,
+                                      0 if words is None else int(words[b, i]))
+                for i in range(ql)]
+        union = np.unique(np.concatenate(rows)) if any(r.size for r in rows) else None
+        if union is None:
+            continue
+        mask = np.zeros((ql, union.size), bool)
+        for i, r in enumerate(rows):
+            mask[i, np.searchsorted(union, r)] = True
+        idx = torch.as_tensor(slot_np(pr.cache_mode, b, union, pr.capacity, pr.block_size,
+                                      block_table, pr.n_sink))
+        Kb = kflat.index_select(0, idx)
+        Vb = vflat.index_select(0, idx)
+        live = mask.any(axis=1)
+        for kvh in range(Hkv):
+            K = to_f64(Kb[:, kvh]) * ks[kvh]
+            V = to_f64(Vb[:, kvh]) * vs[kvh]
+            Q = q64[b, :, kvh * g:(kvh + 1) * g, :].reshape(ql * g, D)
+            S = ((Q @ K.T) * sc).reshape(ql, g, union.size)
+            S = np.where(mask[:, None, :], S, -np.inf)
+            S[~live] = 0.0  # rows with nothing to attend: zeroed below
+            W = np.exp(S - S.max(axis=2, keepdims=True))
+            W /= W.sum(axis=2, keepdims=True)
+            O = (W.reshape(ql * g, union.size) @ V).reshape(ql, g, D)
+            O[~live] = 0.0
+            out[b, :, kvh * g:(kvh + 1) * g, :] = O
+    return out
+
+
 def full_causal_np(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
     """Full T x T causal attention recomputed from scratch (the O(N^2) decoder of the
     lesson's problem statement).  Q, K, V: [T, H, D] float64 -> [T, H, D]."""

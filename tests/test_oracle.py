@@ -461,6 +461,30 @@ def test_c_oracle_equals_numpy_twin(name):
     assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
 
 
+def _all_small_cases():
+    cases = dict(workloads.small_variants())
+    for more in (workloads.small_prefill_variants(), workloads.small_tree_variants(),
+                 workloads.small_fp8_variants()):
+        cases.update(more)
+    return cases
+
+
+@pytest.mark.parametrize("name", list(_all_small_cases()))
+def test_matrix_form_equals_c_oracle(name):
+    """The matrix form of the definition (whole blocks of query rows against a
+    sequence's attended positions with library float64 products, explicit mask) and the
+    C oracle (row by row, position by position) agree on every reduced case: causal,
+    sink/window, token-tree masks, all three cache forms, 8-bit caches, prefill chunks."""
+    case = _all_small_cases()[name]
+    inp = workloads.make_inputs(case)
+    args = (case, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["seq_lens"])
+    kw = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"], tree_mask=inp["tree_mask"])
+    a = oracle.decode(*args, **kw)
+    b = oracle.decode_matmul_np(*args, **kw)
+    assert np.isfinite(b).all()
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("name", list(workloads.small_fp8_variants()))
 def test_fp8_cache_c_oracle_equals_dequantized_twin(name):
     """8-bit caches: the C oracle (bit-definition decoder, dequantise, attend) and the
