@@ -13,7 +13,7 @@
  * (dothoosh.com speculative-decoding article, "verify phase"); q_len in the
  * hundreds is a chunk of a prefill against the cached prefix (the lesson's
  * FlashAttention section: query tiles against key/value tiles, softmax kept
- * running), the rows then run in blocks of 64 on the matrix cores.
+ * running), the rows then run in blocks of up to 256 on the matrix cores.
  *
  * Cache forms:
  *   CONTIGUOUS  each sequence owns `capacity` consecutive slots; position p is slot p.
@@ -52,7 +52,11 @@
  * caller and must stay valid until the work enqueued on the handle's stream has
  * finished.  The handle owns one device workspace, allocated by kvattn_create;
  * kvattn_decode never allocates, never synchronises and never copies to the host,
- * so a call can be captured into a HIP graph.
+ * so a call can be captured into a HIP graph and replayed: the decode step of the
+ * dothoosh.com Moondream article ("Mechanism one: the ping-pong slot system") avoids
+ * runtime device allocation because it synchronises the device, and keeps its
+ * buffers at fixed addresses so the step can be recorded once as a graph and
+ * replayed.
  *
  * Errors: every entry point returns KVATTN_OK (0) or a negative code and never
  * aborts; kvattn_last_error() gives the text of the calling thread's last error.
@@ -60,7 +64,8 @@
  * host: the kernels clamp T to what the cache can hold (CONTIGUOUS/PAGED: T <=
  * capacity) and skip page-table entries outside [0, num_blocks), so they never
  * read outside the caller's buffers; a row with no attended position (T < q_len)
- * gets zeros.
+ * gets zeros.  Handles created with KVATTN_FLAG_DEBUG also record such values
+ * on the device, for kvattn_check to report.
  *
  * Threads: one handle serves one stream; concurrent decode calls on one handle
  * race on its workspace.  Use one handle per in-flight step.
@@ -86,7 +91,8 @@ enum kvattn_status {
     KVATTN_ERR_INVALID_ARG = -1,   /* null pointer, bad enum, inconsistent sizes */
     KVATTN_ERR_UNSUPPORTED = -2,   /* dtype / head_dim / mode combination not built */
     KVATTN_ERR_CAPACITY = -3,      /* batch or q_len beyond what the handle was created for */
-    KVATTN_ERR_HIP = -4            /* a HIP runtime call failed (text in kvattn_last_error) */
+    KVATTN_ERR_HIP = -4,           /* a HIP runtime call failed (text in kvattn_last_error) */
+    KVATTN_ERR_DEVICE_DATA = -5    /* kvattn_check: device-resident arguments were out of range */
 };
 
 enum kvattn_dtype { KVATTN_F32 = 0, KVATTN_F16 = 1, KVATTN_BF16 = 2, KVATTN_FP8_E4M3 = 3 };
@@ -125,10 +131,22 @@ typedef struct kvattn_config {
  *   where a paged cache keeps them. */
 #define KVATTN_FLAG_DETERMINISTIC 1u
 
+/* KVATTN_FLAG_DEBUG: every decode and append first enqueues a check of its
+ *   device-resident arguments - seq_lens (T < 0, or T > capacity for CONTIGUOUS and
+ *   PAGED caches), the page-table entries of pages 0 .. ceil(T / block_size) - 1
+ *   (a block id outside [0, num_blocks)) and token-tree words (bits at or beyond
+ *   q_len) - and records what it finds in a word of the workspace, which
+ *   kvattn_check reads.  Without the flag the same values are clamped or skipped by
+ *   the kernels silently.  Costs one small extra launch per call. */
+#define KVATTN_FLAG_DEBUG 2u
+
 typedef struct kvattn_handle kvattn_handle;
 
 /* Validate `cfg`, plan the work decomposition and allocate the handle's device
- * workspace (split partials) on the current HIP device.  *out is NULL on error. */
+ * workspace (split partials, merge counters) on the current HIP device.  This is the
+ * only call that allocates device memory: later calls reuse the workspace at its
+ * fixed address (the no-runtime-allocation, fixed-buffer rule of the Moondream
+ * article's ping-pong slot system, dothoosh.com).  *out is NULL on error. */
 KVATTN_API int kvattn_create(const kvattn_config* cfg, kvattn_handle** out);
 
 /*
@@ -199,13 +217,20 @@ KVATTN_API int kvattn_decode_tree(kvattn_handle* h, const void* q, const void* k
                                   const uint64_t* tree_mask, void* out);
 
 /* Free the workspace and the handle.  NULL is a no-op.  No enqueued decode may
- * still be using the handle. */
+ * still be using the handle (as a ping-pong slot of the Moondream article is released
+ * only once the step that used it has completed). */
 KVATTN_API void kvattn_destroy(kvattn_handle* h);
 
-/* Stream for later decode calls (a hipStream_t; NULL = the null stream). */
+/* Stream for later decode calls (a hipStream_t; NULL = the null stream).  A handle's
+ * workspace serves one step at a time: calls on one handle are ordered by its one
+ * stream.  Two steps in flight at once (the two alternating slots of the Moondream
+ * article's ping-pong system) take two handles, each with its own workspace, on one
+ * stream or on two.  Switch a handle's stream only once its earlier work is done. */
 KVATTN_API int kvattn_set_stream(kvattn_handle* h, void* stream);
 
-/* Batch for later decode calls, 0 .. max_batch (0 enqueues nothing). */
+/* Batch for later decode calls, 0 .. max_batch (0 enqueues nothing).  Host-side
+ * state only: no device work, no allocation (sizes stay within what kvattn_create
+ * allocated for max_batch). */
 KVATTN_API int kvattn_set_batch(kvattn_handle* h, int32_t batch);
 
 /* Dequantisation scales of an 8-bit cache (kv_dtype KVATTN_FP8_E4M3): float32
@@ -230,6 +255,29 @@ KVATTN_API int kvattn_plan(kvattn_handle* h, int32_t q_len, int32_t mask_mode, i
 
 /* Device bytes kvattn_create would allocate for `cfg`. */
 KVATTN_API int kvattn_workspace_bytes(const kvattn_config* cfg, size_t* bytes);
+
+/*
+ * Debug handles (KVATTN_FLAG_DEBUG): wait for the handle's stream, then report and
+ * clear the validation word the step's checks wrote since the last kvattn_check.
+ * KVATTN_OK if every checked value was in range; KVATTN_ERR_DEVICE_DATA otherwise
+ * (kvattn_last_error names the kinds of bad values: lengths, block ids, tree bits -
+ * the page table maps logical pages to physical blocks and is the caller's data,
+ * nextadmin.net lesson "KV cache and Flash Attention", section "PagedAttention").
+ * KVATTN_ERR_INVALID_ARG for a handle without the flag.  Synchronises: not for use
+ * under graph capture.
+ */
+KVATTN_API int kvattn_check(kvattn_handle* h);
+
+/*
+ * Measurement yardstick (no handle): enqueue on `stream` (a hipStream_t, NULL = the
+ * null stream) one plain streaming read of `bytes` bytes at the device pointer `buf`
+ * (16-byte aligned, bytes a multiple of 16), every byte loaded once.  A decode step
+ * is bounded below by its bytes / the device's bandwidth (dothoosh.com
+ * speculative-decoding article, "The memory-bandwidth wall"); timing this read gives
+ * the bandwidth a read-only stream reaches in practice.  `sink`: one device uint32,
+ * written only when the fold of the data hits one particular value.  No allocation.
+ */
+KVATTN_API int kvattn_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Text of the calling thread's last error ("" if none). */
 KVATTN_API const char* kvattn_last_error(void);

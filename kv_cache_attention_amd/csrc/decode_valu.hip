@@ -38,7 +38,7 @@ const void* select_valu_kernel(int dtype, int kv_dtype, int head_dim, int rows, 
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int kv_dtype, int head_dim,
                               int grid, hipStream_t st) {
     const void* k = select_valu_kernel(dtype, kv_dtype, head_dim, p.rows, p.cache_mode,
-                                       p.q_len > 1 || p.mask_mode == MASK_TREE);
+                                       valu_masked(p.q_len, p.mask_mode));
     if (!k) return hipErrorInvalidValue;
     DecodeParams pp = p;
     void* args[] = {&pp};

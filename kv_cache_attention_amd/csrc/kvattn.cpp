@@ -69,7 +69,7 @@ struct kvattn_handle {
     kvattn_config cfg;
     int device;
     int num_cus;
-    int resident[kMaxQLen + 1];  // per q_len: workgroups of its kernel instance resident at once
+    int resident[kMaxQLen + 1][2];  // per (q_len, masked instance): workgroups resident at once
     hipStream_t stream;
     int32_t batch;
     int32_t forced_chunk;
@@ -78,6 +78,7 @@ struct kvattn_handle {
     float* ws;              // partials: acc [ws_floats], (m, l), then the arrival counters
     int64_t ws_part_rows;   // partial rows (slot x segment row) the workspace holds
     int64_t n_units;        // arrival counters (batch x segments per sequence)
+    uint32_t* vword;        // debug validation word (after the counters and the unit queue)
     int64_t stride_seq, stride_head, stride_tok;
 };
 
@@ -156,7 +157,7 @@ int validate_config(const kvattn_config* c) {
         return fail(KVATTN_ERR_UNSUPPORTED, "kv_dtype must be 0, dtype or FP8_E4M3");
     if (c->kv_dtype == KVATTN_FP8_E4M3 && c->dtype != KVATTN_F16 && c->dtype != KVATTN_BF16)
         return fail(KVATTN_ERR_UNSUPPORTED, "8-bit caches need F16 or BF16 queries");
-    if (c->flags & ~KVATTN_FLAG_DETERMINISTIC)
+    if (c->flags & ~(KVATTN_FLAG_DETERMINISTIC | KVATTN_FLAG_DEBUG))
         return fail(KVATTN_ERR_INVALID_ARG, "unknown flag bits");
     if (!(c->scale >= 0.0f) || std::isinf(c->scale))
         return fail(KVATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
@@ -210,14 +211,14 @@ int validate_decode_args(const kvattn_handle* h, int32_t q_len, int32_t mask_mod
 
 // Workgroups of the kernel instance a decode with q_len would launch that fit on
 // the device at once (occupancy query).
-int resident_for(const kvattn_config& c, int q_len, int num_cus) {
+int resident_for(const kvattn_config& c, int q_len, bool masked, int num_cus) {
     const int rows = rows_of(c, q_len);
     const bool prefill = use_prefill(c, q_len);
     const bool mfma = use_mfma(c, q_len);
     const void* k = prefill ? kvattn::select_prefill_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
                     : mfma  ? kvattn::select_mfma_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
                             : kvattn::select_valu_kernel(c.dtype, kv_dtype_of(c), c.head_dim, rows,
-                                                         c.cache_mode, q_len > 1);
+                                                         c.cache_mode, masked);
     const int threads = prefill ? kvattn::kPrefillThreads
                         : mfma  ? kvattn::kMfmaThreads
                                 : kvattn::valu_threads(rows);
@@ -228,9 +229,10 @@ int resident_for(const kvattn_config& c, int q_len, int num_cus) {
     return std::min(per_cu * num_cus, kMaxResidentWorkgroups);
 }
 
-int resident_workgroups(kvattn_handle* h, int q_len) {
-    int& r = h->resident[q_len];
-    if (r <= 0) r = resident_for(h->cfg, q_len, h->num_cus);
+int resident_workgroups(kvattn_handle* h, int q_len, int mask_mode) {
+    const bool masked = kvattn::valu_masked(q_len, mask_mode);
+    int& r = h->resident[q_len][masked ? 1 : 0];
+    if (r <= 0) r = resident_for(h->cfg, q_len, masked, h->num_cus);
     return r;
 }
 
@@ -256,10 +258,11 @@ int64_t workspace_part_rows(const kvattn_config& c) {
     return best;
 }
 
-// acc and (m, l) of the partials, one arrival counter per segment, the unit queue.
+// acc and (m, l) of the partials, one arrival counter per segment, the unit queue
+// (two words), the debug validation word.
 size_t workspace_size(const kvattn_config& c, int64_t part_rows) {
     return (size_t)part_rows * (size_t)(c.head_dim + 2) * sizeof(float) +
-           (size_t)(counter_units(c) + 2) * sizeof(int32_t);
+           (size_t)(counter_units(c) + 3) * sizeof(int32_t);
 }
 
 // Grid and minimum unit length of a decode with these host arguments.  The work
@@ -273,7 +276,7 @@ int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
     *min_chunk = h->forced_chunk > 0 ? h->forced_chunk
                                      : (use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk);
     const int64_t units_max = ceil_div(w_max, *min_chunk);  // units are >= min_chunk
-    const int64_t g = std::min<int64_t>(resident_workgroups(h, q_len), units_max);
+    const int64_t g = std::min<int64_t>(resident_workgroups(h, q_len, mask_mode), units_max);
     const int64_t units = h->forced_chunk > 0
                               ? units_max
                               : std::min<int64_t>(units_max + 1, g * (kUnitsPerWg + kTailUnits));
@@ -290,6 +293,41 @@ int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
 extern "C" {
 
 const char* kvattn_last_error(void) { return g_last_error.c_str(); }
+
+int kvattn_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(KVATTN_ERR_INVALID_ARG, "buf and sink must be non-NULL");
+    if (!aligned16(buf) || bytes % 16)
+        return fail(KVATTN_ERR_INVALID_ARG, "buf must be 16-byte aligned and bytes a multiple of 16");
+    if (bytes == 0) return KVATTN_OK;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = kvattn::launch_stream_read(buf, (int64_t)bytes, sink, cus,
+                                       reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVATTN_ERR_HIP, std::string("stream read: ") + hipGetErrorString(e));
+    return KVATTN_OK;
+}
+
+int kvattn_check(kvattn_handle* h) {
+    if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
+    if (!(h->cfg.flags & KVATTN_FLAG_DEBUG))
+        return fail(KVATTN_ERR_INVALID_ARG, "kvattn_check needs a handle created with KVATTN_FLAG_DEBUG");
+    uint32_t w = 0;
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e == hipSuccess) e = hipMemcpy(&w, h->vword, sizeof(w), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && w) {
+        e = hipMemsetAsync(h->vword, 0, sizeof(w), h->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+    }
+    if (e != hipSuccess) return fail(KVATTN_ERR_HIP, std::string("kvattn_check: ") + hipGetErrorString(e));
+    if (!w) return KVATTN_OK;
+    std::string msg = "device-resident arguments out of range since the last check:";
+    if (w & kvattn::VALIDATE_SEQ_LEN) msg += " seq_lens (negative, or above capacity)";
+    if (w & kvattn::VALIDATE_BLOCK_ID) msg += " block_table (block ids outside [0, num_blocks))";
+    if (w & kvattn::VALIDATE_TREE_BITS) msg += " tree_mask (bits at or beyond q_len)";
+    return fail(KVATTN_ERR_DEVICE_DATA, msg);
+}
 
 int kvattn_workspace_bytes(const kvattn_config* cfg, size_t* bytes) {
     int rc = validate_config(cfg);
@@ -329,7 +367,7 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
         delete h;
         return fail(KVATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     }
-    for (int& r : h->resident) r = 0;
+    for (auto& r : h->resident) r[0] = r[1] = 0;
     h->ws_part_rows = workspace_part_rows(*cfg);
     h->n_units = counter_units(*cfg);
     // the merge addresses partials with 32-bit byte offsets
@@ -351,6 +389,8 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
         delete h;
         return fail(KVATTN_ERR_HIP, std::string("hipMemset(workspace): ") + hipGetErrorString(e));
     }
+    h->vword = reinterpret_cast<uint32_t*>(reinterpret_cast<int32_t*>(
+                   h->ws + h->ws_part_rows * (cfg->head_dim + 2)) + h->n_units + 2);
     *out = h;
     return KVATTN_OK;
 }
@@ -542,6 +582,31 @@ int prepare_append(kvattn_handle* h, const void* k_new, const void* v_new, void*
     return KVATTN_OK;
 }
 
+// Handles created with KVATTN_FLAG_DEBUG: enqueue the check of the step's
+// device-resident arguments (lengths, page-table entries, tree words) ahead of its
+// kernels; kvattn_check reports what it found.
+int maybe_validate(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,
+                   int32_t q_len, const uint64_t* tree) {
+    const kvattn_config& c = h->cfg;
+    if (!(c.flags & KVATTN_FLAG_DEBUG) || h->batch == 0) return KVATTN_OK;
+    kvattn::ValidateParams v;
+    v.seq_lens = seq_lens;
+    v.block_table = c.cache_mode == KVATTN_PAGED ? block_table : nullptr;
+    v.tree_mask = tree;
+    v.word = h->vword;
+    v.batch = h->batch;
+    v.q_len = q_len;
+    v.cache_mode = c.cache_mode;
+    v.capacity = c.capacity;
+    v.log2_block = c.cache_mode == KVATTN_PAGED ? ilog2(c.block_size) : 0;
+    v.num_blocks = c.cache_mode == KVATTN_PAGED ? c.num_blocks : 0;
+    v.blocks_per_seq = c.cache_mode == KVATTN_PAGED ? c.capacity / c.block_size : 0;
+    const hipError_t e = kvattn::launch_validate(v, h->stream);
+    if (e != hipSuccess)
+        return fail(KVATTN_ERR_HIP, std::string("validation launch: ") + hipGetErrorString(e));
+    return KVATTN_OK;
+}
+
 int launch_append(kvattn_handle* h, const kvattn::AppendParams& a) {
     hipError_t e = kvattn::launch_append(a, h->stream);
     if (e != hipSuccess)
@@ -561,6 +626,7 @@ int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const vo
     int rc = prepare_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len, mask_mode,
                             n_sink, window, out, p, &grid);
     if (rc) return rc;
+    if (grid > 0 && (rc = maybe_validate(h, block_table, seq_lens, q_len, nullptr))) return rc;
     return launch_decode(h, p, grid, q_len);
 }
 
@@ -573,6 +639,7 @@ int kvattn_decode_tree(kvattn_handle* h, const void* q, const void* k_cache, con
     int rc = prepare_decode(h, q, k_cache, v_cache, block_table, seq_lens, q_len,
                             KVATTN_MASK_TREE, 0, 0, out, p, &grid, tree_mask);
     if (rc) return rc;
+    if (grid > 0 && (rc = maybe_validate(h, block_table, seq_lens, q_len, tree_mask))) return rc;
     return launch_decode(h, p, grid, q_len);
 }
 
@@ -583,7 +650,9 @@ int kvattn_append(kvattn_handle* h, const void* k_new, const void* v_new, void* 
     int rc = prepare_append(h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len,
                             n_sink, &a);
     if (rc) return rc;
-    return a.n_chunks > 0 ? launch_append(h, a) : KVATTN_OK;
+    if (a.n_chunks == 0) return KVATTN_OK;
+    if ((rc = maybe_validate(h, block_table, seq_lens, q_len, nullptr))) return rc;
+    return launch_append(h, a);
 }
 
 int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new, const void* v_new,
@@ -600,6 +669,9 @@ int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new, con
     rc = prepare_append(h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len,
                         mask_mode == KVATTN_MASK_SINK_WINDOW ? n_sink : 0, &a);
     if (rc) return rc;
+    if ((a.n_chunks > 0 || grid > 0) &&
+        (rc = maybe_validate(h, block_table, seq_lens, q_len, nullptr)))
+        return rc;
     if (a.n_chunks > 0) {
         rc = launch_append(h, a);
         if (rc) return rc;

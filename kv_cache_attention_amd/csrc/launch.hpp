@@ -11,6 +11,10 @@ namespace kvattn {
 // `grid` workgroups share the step's work in equal slices.
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int kv_dtype, int head_dim,
                               int grid, hipStream_t st);
+// The vector-ALU instance tests each score against its row's mask when the rows of a
+// sequence attend different sets: q_len > 1, or any token-tree decode.  The launch and
+// the occupancy query that sizes its grid both go through this predicate.
+inline bool valu_masked(int q_len, int mask_mode) { return q_len > 1 || mask_mode == MASK_TREE; }
 int valu_rows_per_block(int rows);
 int valu_threads(int rows);  // workgroup size of the instance serving `rows`
 // kv_dtype: element type of the caches (FP8 = 8-bit E4M3 codes, with F16/BF16 queries)
@@ -48,6 +52,22 @@ const void* select_prefill_kernel(int dtype, int head_dim, int rows, int cache_m
 #endif
 constexpr int kPrefillThreads = KVATTN_PF_WAVES * 64;
 constexpr int kPrefillRows = KVATTN_PF_WAVES * KVATTN_PF_RW * 16;
+
+// Debug validation of seq_lens, the page table and token-tree words (handles created
+// with KVATTN_FLAG_DEBUG): bits of *word are set for each kind of bad value found.
+enum : uint32_t { VALIDATE_SEQ_LEN = 1u, VALIDATE_BLOCK_ID = 2u, VALIDATE_TREE_BITS = 4u };
+struct ValidateParams {
+    const int32_t* seq_lens;
+    const int32_t* block_table;  // PAGED only
+    const uint64_t* tree_mask;   // token-tree decodes only
+    uint32_t* word;              // the handle's validation word (device)
+    int32_t batch, q_len, cache_mode, capacity, log2_block, num_blocks, blocks_per_seq;
+};
+hipError_t launch_validate(const ValidateParams& v, hipStream_t st);
+
+// Measurement: a plain streaming read of `bytes` (a multiple of 16) at `buf`.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int num_cus,
+                              hipStream_t st);
 
 // Test entry: the slots each new row attends, through the kernels' own gather code.
 hipError_t launch_debug_gather(const DecodeParams& p, int max_slots, int32_t* slots_out,

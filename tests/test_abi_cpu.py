@@ -69,7 +69,19 @@ def test_null_handle_is_rejected():
     assert lib.kvattn_set_stream(None, None) == -1
     assert lib.kvattn_set_split_len(None, 64) == -1
     assert lib.kvattn_plan(None, 1, 0, 0, 0, None, None, None) == -1
+    assert lib.kvattn_check(None) == -1
     lib.kvattn_destroy(None)  # no-op
+
+
+def test_flags_are_validated():
+    lib = kb.load()
+    h = ctypes.c_void_p()
+    cfg = _cfg()
+    cfg.flags = 4  # no such flag
+    assert lib.kvattn_create(ctypes.byref(cfg), ctypes.byref(h)) == -1
+    assert not h.value
+    # the debug flag is known (creation itself needs a device, checked on the GPU)
+    assert kb.kvattn_workspace_bytes(_cfg(debug=True, deterministic=True)) > 0
 
 
 def test_workspace_bytes_is_host_only_and_bounded():

@@ -137,8 +137,8 @@ def test_append_argument_errors():
     with pytest.raises(kb.KVAttnError):   # ring: n_sink + q_len > capacity
         h.append(kn, vn, inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 1,
                  case.capacity)
-    with pytest.raises(kb.KVAttnError):   # q_len above max_q_len
-        h.append(kn, vn, inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 99, 4)
+    with pytest.raises(kb.KVAttnError):   # q_len above max_q_len (the C ABI's own check)
+        kb.kvattn_append(h.h, kn, vn, inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 99, 4)
     with pytest.raises(ValueError):       # element type of the new rows
         h.append(kn.float(), vn.float(), inp["k_cache"], inp["v_cache"], None, inp["seq_lens"],
                  1, 4)

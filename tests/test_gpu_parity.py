@@ -158,7 +158,7 @@ def test_gather_indices_are_bit_exact(name):
     h = kb.KVAttn.for_case(case)
     max_slots = case.capacity
     slots, counts = h.debug_gather(d["block_table"], d["seq_lens"], case.q_len, case.mask_mode,
-                                   case.n_sink, case.window, max_slots, batch=case.batch)
+                                   case.n_sink, case.window, max_slots)
     slots, counts = slots.cpu().numpy(), counts.cpu().numpy()
     for b in range(case.batch):
         for i in range(case.q_len):
@@ -176,7 +176,7 @@ def test_ring_gather_edges(T, q_len):
     sl = torch.tensor([T], dtype=torch.int32)
     h = kb.KVAttn.for_case(SINK)
     slots, counts = h.debug_gather(None, sl.cuda(), q_len, case.mask_mode, case.n_sink,
-                                   case.window, case.capacity, batch=1)
+                                   case.window, case.capacity)
     slots, counts = slots.cpu().numpy(), counts.cpu().numpy()
     for i in range(q_len):
         _, ref = oracle.attended(case, None, sl, 0, i)
@@ -236,9 +236,9 @@ def test_host_side_errors_with_a_device():
     with pytest.raises(kb.KVAttnError) as e:   # ring needs the sink/window mask
         h.decode(inp["q"], inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 1, "causal")
     assert e.value.code == -1
-    with pytest.raises(kb.KVAttnError) as e:   # q_len beyond the handle
-        h.decode(inp["q"], inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 2,
-                 "sink_window", 4, 300)
+    with pytest.raises(kb.KVAttnError) as e:   # q_len beyond the handle (the C ABI's own check)
+        kb.kvattn_decode(h.h, inp["q"], inp["k_cache"], inp["v_cache"], None, inp["seq_lens"], 2,
+                         kb.MASK["sink_window"], 4, 300, torch.empty_like(inp["q"]))
     assert e.value.code == -3
     with pytest.raises(kb.KVAttnError) as e:
         h.set_batch(case.batch + 1)

@@ -81,7 +81,7 @@ def test_tree_gather_is_bit_exact(name):
     max_slots = case.capacity + 1
     h = kb.KVAttn.for_case(case)
     slots, counts = h.debug_gather_tree(d["block_table"], d["seq_lens"], case.q_len,
-                                        d["tree_mask"], max_slots, batch=case.batch)
+                                        d["tree_mask"], max_slots)
     torch.cuda.synchronize()
     slots, counts = slots.cpu().numpy(), counts.cpu().numpy()
     words = oracle.tree_words(inp["tree_mask"])
