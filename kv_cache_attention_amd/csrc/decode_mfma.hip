@@ -120,7 +120,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             const int64_t off = row_offset(p, L, kvh) + lq * 8;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[tt][ks] = *reinterpret_cast<const u32x4*>(kp + off + ks * 32);
+                kf[tt][ks] = load_stream<u32x4>(kp + off + ks * 32);
         }
     };
     // V coalesced: load v covers PPI whole rows, lane l -> row v*PPI + l/CPR, chunk l%CPR.
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
             vok[v] = L.unit >= 0;
             L.unit = L.unit >= 0 ? L.unit : 0;
-            vf[v] = *reinterpret_cast<const u32x4*>(vp + row_offset(p, L, kvh) + (l % CPR) * 8);
+            vf[v] = load_stream<u32x4>(vp + row_offset(p, L, kvh) + (l % CPR) * 8);
         }
     };
 

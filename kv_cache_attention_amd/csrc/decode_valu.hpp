@@ -343,9 +343,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             if constexpr (CACHE == PAGED) fetch_pages(x, wave, blk);
             address(x, wave);
 #pragma unroll
-            for (int u = 0; u < U; ++u) kwA[u] = *reinterpret_cast<const KVT*>(ka[u]);
+            for (int u = 0; u < U; ++u) kwA[u] = load_stream<KVT>(ka[u]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) vwA[u] = *reinterpret_cast<const KVT*>(ka[u] + dv);
+            for (int u = 0; u < U; ++u) vwA[u] = load_stream<KVT>(ka[u] + dv);
         }
     };
 
@@ -466,9 +466,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
                 if (n2 < n_tiles) fetch_pages(x, n2, blk);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) kn[u] = *reinterpret_cast<const KVT*>(ka[u]);
+            for (int u = 0; u < U; ++u) kn[u] = load_stream<KVT>(ka[u]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) vn[u] = *reinterpret_cast<const KVT*>(ka[u] + dv);
+            for (int u = 0; u < U; ++u) vn[u] = load_stream<KVT>(ka[u] + dv);
             float pw[ROWS][U];
 #pragma unroll
             for (int r = 0; r < ROWS; ++r) {

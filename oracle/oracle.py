@@ -51,14 +51,16 @@ class _Problem(ctypes.Structure):
 
 
 def load():
-    """Load (building first if absent) the C oracle."""
+    """Load (building first if absent) the C oracle.  KVATTN_ORACLE_LIB names another
+    build of it (the mutation test points the pins at deliberately broken copies)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = os.environ.get("KVATTN_ORACLE_LIB") or _LIB_PATH
+    if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
         from . import build as _b
         _b.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER(_Problem)
     vp, i32p, f64p, i64p = (ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64))
