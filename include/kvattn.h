@@ -216,6 +216,29 @@ KVATTN_API int kvattn_decode_tree(kvattn_handle* h, const void* q, const void* k
                                   const int32_t* seq_lens, int32_t q_len,
                                   const uint64_t* tree_mask, void* out);
 
+/*
+ * kvattn_decode without a handle and without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same operation, arguments, layouts and kernels as
+ * kvattn_decode (the configuration in `cfg`, the batch and the stream given per call);
+ * the step's partials, arrival counters and unit queue live in a static 32 MiB device
+ * array that each GPU holds from the library's load until the process ends.
+ *   cfg          as for kvattn_create; 16-bit or fp32 caches (kv_dtype 0 or dtype),
+ *                no KVATTN_FLAG_DEBUG
+ *   batch        0 .. cfg->max_batch
+ *   stream       hipStream_t (NULL = the null stream)
+ * KVATTN_ERR_CAPACITY, with nothing enqueued, when the step needs more than the array
+ * holds: more than 65,536 segments (batch x KV heads x row blocks) or partials beyond
+ * 32 MiB (the decode and verify shapes fit; large prefill chunks need a handle).
+ * All calls on one GPU share its array, so calls that overlap on one GPU race: order
+ * them on one stream.  Never allocates, never synchronises.
+ */
+KVATTN_API int kvattn_decode_noalloc(const kvattn_config* cfg, int32_t batch, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     int32_t q_len, int32_t mask_mode, int32_t n_sink,
+                                     int32_t window, void* out, void* stream);
+
 /* Free the workspace and the handle.  NULL is a no-op.  No enqueued decode may
  * still be using the handle (as a ping-pong slot of the Moondream article is released
  * only once the step that used it has completed). */

@@ -30,7 +30,7 @@ EXPORTS = ("kvattn_create", "kvattn_decode", "kvattn_destroy", "kvattn_set_strea
            "kvattn_set_batch", "kvattn_set_split_len", "kvattn_set_kv_scales", "kvattn_plan",
            "kvattn_workspace_bytes", "kvattn_last_error", "kvattn_debug_gather", "kvattn_append",
            "kvattn_append_decode", "kvattn_decode_tree", "kvattn_debug_gather_tree",
-           "kvattn_check", "kvattn_stream_read")
+           "kvattn_check", "kvattn_stream_read", "kvattn_decode_noalloc")
 
 
 class kvattn_config(ctypes.Structure):
@@ -98,6 +98,9 @@ def load() -> ctypes.CDLL:
     lib.kvattn_check.restype = ctypes.c_int
     lib.kvattn_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.kvattn_stream_read.restype = ctypes.c_int
+    lib.kvattn_decode_noalloc.argtypes = [ctypes.POINTER(kvattn_config), i32, vp, vp, vp, vp, vp,
+                                          i32, i32, i32, i32, vp, vp]
+    lib.kvattn_decode_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -227,6 +230,17 @@ def kvattn_last_error() -> str:
 
 def kvattn_check(h) -> None:
     _check(load().kvattn_check(h), "kvattn_check")
+
+
+def kvattn_decode_noalloc(cfg: kvattn_config, batch: int, q, k_cache, v_cache, block_table,
+                          seq_lens, q_len: int, mask_mode: int, n_sink: int, window: int, out,
+                          stream: int) -> None:
+    _check(load().kvattn_decode_noalloc(ctypes.byref(cfg), batch, _dev_ptr(q, "q"),
+                                        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                        _dev_ptr(block_table, "block_table"),
+                                        _dev_ptr(seq_lens, "seq_lens"), q_len, mask_mode, n_sink,
+                                        window, _dev_ptr(out, "out"), ctypes.c_void_p(stream)),
+           "kvattn_decode_noalloc")
 
 
 def kvattn_stream_read(buf, sink, stream: int) -> None:

@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -75,10 +76,13 @@ struct kvattn_handle {
     int32_t forced_chunk;
     const float* k_scale;   // 8-bit caches: per-KV-head dequantisation scales (device)
     const float* v_scale;
-    float* ws;              // partials: acc [ws_floats], (m, l), then the arrival counters
+    float* ws;              // partials: acc [ws_part_rows, D] (the handle's allocation starts here)
+    float* ws_ml;           // partials: (m, l) [ws_part_rows, 2]
+    int32_t* counters;      // arrival counters, one per segment, zero between calls
+    int32_t* queue;         // unit queue: two words, zero between calls
     int64_t ws_part_rows;   // partial rows (slot x segment row) the workspace holds
-    int64_t n_units;        // arrival counters (batch x segments per sequence)
-    uint32_t* vword;        // debug validation word (after the counters and the unit queue)
+    int64_t n_units;        // arrival counters available (batch x segments per sequence)
+    uint32_t* vword;        // debug validation word (NULL without a workspace for it)
     int64_t stride_seq, stride_head, stride_tok;
 };
 
@@ -277,13 +281,19 @@ int plan_for(kvattn_handle* h, int32_t q_len, int32_t mask_mode, int32_t n_sink,
                                      : (use_mfma(c, q_len) ? kMinChunkMfma : kMinChunk);
     const int64_t units_max = ceil_div(w_max, *min_chunk);  // units are >= min_chunk
     const int64_t g = std::min<int64_t>(resident_workgroups(h, q_len, mask_mode), units_max);
+    // units of the step: exactly min_chunk long when forced; otherwise at most
+    // kUnitsPerWg per workgroup (plus the tail's, when there is one) and one more for
+    // the rounding of the unit length
     const int64_t units = h->forced_chunk > 0
                               ? units_max
-                              : std::min<int64_t>(units_max + 1, g * (kUnitsPerWg + kTailUnits));
+                              : std::min<int64_t>(units_max + 1,
+                                                  g * (kUnitsPerWg + (kTailPct > 0 ? kTailUnits : 0)) + 1);
     const int64_t need =
         (units + (int64_t)h->batch * segs_per_seq_of(c, q_len)) * seg_rows_of(c, q_len);
     if (need > h->ws_part_rows)
-        return fail(KVATTN_ERR_CAPACITY, "unit count exceeds the handle's workspace");
+        return fail(KVATTN_ERR_CAPACITY, "unit count exceeds the workspace");
+    if ((int64_t)h->batch * segs_per_seq_of(c, q_len) > h->n_units)
+        return fail(KVATTN_ERR_CAPACITY, "segment count exceeds the workspace's arrival counters");
     *grid = (int)std::max<int64_t>(1, g);
     return KVATTN_OK;
 }
@@ -337,13 +347,13 @@ int kvattn_workspace_bytes(const kvattn_config* cfg, size_t* bytes) {
     return KVATTN_OK;
 }
 
-int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
-    if (!out) return fail(KVATTN_ERR_INVALID_ARG, "out is NULL");
-    *out = nullptr;
-    int rc = validate_config(cfg);
-    if (rc) return rc;
-    kvattn_handle* h = new (std::nothrow) kvattn_handle();
-    if (!h) return fail(KVATTN_ERR_INVALID_ARG, "host allocation failed");
+}  // extern "C"
+
+namespace {
+
+// Host-side state of a handle that does not depend on where its workspace lives:
+// configuration, cache strides, the current device and its compute-unit count.
+int init_handle(kvattn_handle* h, const kvattn_config* cfg) {
     h->cfg = *cfg;
     h->stream = nullptr;
     h->batch = cfg->max_batch;
@@ -363,11 +373,35 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
     hipError_t e = hipGetDevice(&h->device);
     if (e == hipSuccess)
         e = hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
-    if (e != hipSuccess) {
-        delete h;
-        return fail(KVATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
-    }
+    if (e != hipSuccess) return fail(KVATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     for (auto& r : h->resident) r[0] = r[1] = 0;
+    h->ws = nullptr;
+    h->ws_ml = nullptr;
+    h->counters = nullptr;
+    h->queue = nullptr;
+    h->vword = nullptr;
+    h->ws_part_rows = 0;
+    h->n_units = 0;
+    return KVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
+    if (!out) return fail(KVATTN_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int rc = validate_config(cfg);
+    if (rc) return rc;
+    kvattn_handle* h = new (std::nothrow) kvattn_handle();
+    if (!h) return fail(KVATTN_ERR_INVALID_ARG, "host allocation failed");
+    rc = init_handle(h, cfg);
+    if (rc) {
+        delete h;
+        return rc;
+    }
+    hipError_t e;
     h->ws_part_rows = workspace_part_rows(*cfg);
     h->n_units = counter_units(*cfg);
     // the merge addresses partials with 32-bit byte offsets
@@ -389,8 +423,10 @@ int kvattn_create(const kvattn_config* cfg, kvattn_handle** out) {
         delete h;
         return fail(KVATTN_ERR_HIP, std::string("hipMemset(workspace): ") + hipGetErrorString(e));
     }
-    h->vword = reinterpret_cast<uint32_t*>(reinterpret_cast<int32_t*>(
-                   h->ws + h->ws_part_rows * (cfg->head_dim + 2)) + h->n_units + 2);
+    h->ws_ml = h->ws + h->ws_part_rows * cfg->head_dim;
+    h->counters = reinterpret_cast<int32_t*>(h->ws + h->ws_part_rows * (cfg->head_dim + 2));
+    h->queue = h->counters + h->n_units;
+    h->vword = reinterpret_cast<uint32_t*>(h->queue + 2);
     *out = h;
     return KVATTN_OK;
 }
@@ -457,9 +493,9 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.seq_lens = sl;
     p.out = out;
     p.ws_acc = h->ws;
-    p.ws_ml = h->ws + h->ws_part_rows * c.head_dim;
-    p.counters = reinterpret_cast<int32_t*>(h->ws + h->ws_part_rows * (c.head_dim + 2));
-    p.queue = p.counters + h->n_units;
+    p.ws_ml = h->ws_ml;
+    p.counters = h->counters;
+    p.queue = h->queue;
     p.stride_seq = h->stride_seq;
     p.stride_head = h->stride_head;
     p.stride_tok = h->stride_tok;
@@ -588,7 +624,7 @@ int prepare_append(kvattn_handle* h, const void* k_new, const void* v_new, void*
 int maybe_validate(kvattn_handle* h, const int32_t* block_table, const int32_t* seq_lens,
                    int32_t q_len, const uint64_t* tree) {
     const kvattn_config& c = h->cfg;
-    if (!(c.flags & KVATTN_FLAG_DEBUG) || h->batch == 0) return KVATTN_OK;
+    if (!(c.flags & KVATTN_FLAG_DEBUG) || h->batch == 0 || !h->vword) return KVATTN_OK;
     kvattn::ValidateParams v;
     v.seq_lens = seq_lens;
     v.block_table = c.cache_mode == KVATTN_PAGED ? block_table : nullptr;
@@ -723,6 +759,108 @@ int kvattn_debug_gather_tree(kvattn_handle* h, const int32_t* block_table,
     if (!tree_mask) return fail(KVATTN_ERR_INVALID_ARG, "tree_mask is NULL");
     return debug_gather(h, block_table, seq_lens, q_len, KVATTN_MASK_TREE, 0, 0, tree_mask,
                         max_slots, slots_out, counts_out);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode without allocation
+//
+// For callers that cannot allocate device memory (code under graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): kvattn_decode_noalloc takes no
+// handle.  Its partials, arrival counters and unit queue live in `scratch`, a
+// file-scope device array of kScratchBytes that each GPU holds from the library's load
+// until the process ends.  In host code the array's name is only a stand-in: its
+// device address comes from hipGetSymbolAddress, once per device (with that device
+// current), and that pointer is what the kernels receive.  Layout: the unit queue
+// (two words) at offset 0, kScratchCounters arrival counters at offset 256, the
+// partials after them; every call leaves the queue and the counters at zero, and the
+// array starts zeroed (and is zeroed once more, by a fill kernel, at a device's first
+// call).  Every call on a GPU shares its array: calls that overlap on one GPU race.
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int64_t kScratchCounters = 1 << 16;
+constexpr size_t kScratchHead = 256 + (size_t)kScratchCounters * sizeof(int32_t);
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+// The device address of this device's scratch array (looked up and cleared at the
+// device's first call, on the caller's stream).
+int scratch_of(int device, hipStream_t st, unsigned char** out) {
+    if (device < 0 || device >= kMaxDevices) return fail(KVATTN_ERR_UNSUPPORTED, "device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(KVATTN_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        const int64_t words = (int64_t)(kScratchHead / sizeof(uint32_t));
+        hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, st, static_cast<uint32_t*>(ptr),
+                           words);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(KVATTN_ERR_HIP, std::string("scratch clear: ") + hipGetErrorString(e));
+        g_scratch_ptr[device] = static_cast<unsigned char*>(ptr);
+    }
+    *out = g_scratch_ptr[device];
+    return KVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_decode_noalloc(const kvattn_config* cfg, int32_t batch, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, int32_t q_len, int32_t mask_mode,
+                          int32_t n_sink, int32_t window, void* out, void* stream) {
+    int rc = validate_config(cfg);
+    if (rc) return rc;
+    if (kv_dtype_of(*cfg) == KVATTN_FP8_E4M3)
+        return fail(KVATTN_ERR_UNSUPPORTED, "kvattn_decode_noalloc: 8-bit caches need a handle (scales)");
+    if (cfg->flags & KVATTN_FLAG_DEBUG)
+        return fail(KVATTN_ERR_UNSUPPORTED, "kvattn_decode_noalloc: no debug validation without a handle");
+    if (batch < 0) return fail(KVATTN_ERR_INVALID_ARG, "batch must be >= 0");
+    if (batch > cfg->max_batch) return fail(KVATTN_ERR_CAPACITY, "batch exceeds max_batch");
+    if (q_len < 1) return fail(KVATTN_ERR_INVALID_ARG, "q_len must be >= 1");
+    if (q_len > cfg->max_q_len) return fail(KVATTN_ERR_CAPACITY, "q_len exceeds max_q_len");
+    kvattn_handle h;
+    rc = init_handle(&h, cfg);
+    if (rc) return rc;
+    h.batch = batch;
+    h.stream = reinterpret_cast<hipStream_t>(stream);
+    // what the scratch holds after its head: partial rows of head_dim + 2 floats, and
+    // the arrival counters; the plan is checked against these before anything is enqueued
+    h.ws_part_rows = (int64_t)((kScratchBytes - kScratchHead) /
+                               ((size_t)(cfg->head_dim + 2) * sizeof(float)));
+    h.n_units = kScratchCounters;
+    kvattn::DecodeParams p;
+    int grid;
+    rc = prepare_decode(&h, q, k_cache, v_cache, block_table, seq_lens, q_len, mask_mode, n_sink,
+                        window, out, p, &grid);
+    if (rc == KVATTN_ERR_CAPACITY)
+        return fail(rc, "kvattn_decode_noalloc: the step needs more than the 32 MiB scratch holds (" +
+                            g_last_error + "); use a handle (kvattn_create)");
+    if (rc) return rc;
+    if (grid == 0) return KVATTN_OK;
+    unsigned char* base = nullptr;
+    rc = scratch_of(h.device, h.stream, &base);
+    if (rc) return rc;
+    p.queue = reinterpret_cast<int32_t*>(base);
+    p.counters = reinterpret_cast<int32_t*>(base + 256);
+    p.ws_acc = reinterpret_cast<float*>(base + kScratchHead);
+    p.ws_ml = p.ws_acc + h.ws_part_rows * cfg->head_dim;
+    return launch_decode(&h, p, grid, q_len);
 }
 
 }  // extern "C"
