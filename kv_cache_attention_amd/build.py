@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libkvattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kvattn.cpp", "decode_valu.hip", "valu_f16.hip", "valu_bf16.hip", "valu_f32.hip",
-           "valu_f16_fp8.hip", "valu_bf16_fp8.hip", "decode_mfma.hip", "debug_gather.hip",
+           "valu_f16_fp8.hip", "valu_bf16_fp8.hip", "decode_mfma.hip", "decode_mfma_fp8.hip", "debug_gather.hip",
            "append.hip", "prefill_mfma.hip", "validate.hip",
            "stream_read.hip"]
 

@@ -248,7 +248,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
     __shared__ float sm_acc[NWAVES][ROWS][D];
     __shared__ float sm_ml[NWAVES][ROWS][2];
     __shared__ MergeSmem<ROWS, THREADS> msm;
-    __shared__ int s_next_tile;
+    // the tile counter in word 0; lanes 1 .. 63 of the all-lane atomic below hit words
+    // 1 .. 63 (adding 0), so one atomic never sends 64 lanes to one LDS bank
+    __shared__ int s_tile_words[64];
+    int& s_next_tile = s_tile_words[0];
 
     // Byte addresses: K row of (unit, slot idx) at kb + unit * unit_bytes + idx * tok_bytes
     // (unit = the pool block for paged caches, folded into kb otherwise); V at K + dv.
@@ -403,11 +406,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
         // requested a tile ahead (two for paged caches, whose page-table entries are
         // read as soon as the tile is granted); deterministic mode: every NWAVES-th tile,
         // a fixed summation order.  Every lane takes part in the atomic (lane 0 adds
-        // 1, the others 0), so the loop holds no lane-divergent branch; lane 0's
-        // result is the tile granted.
+        // 1 to the counter, lane l adds 0 to its own word l), so the loop holds no
+        // lane-divergent branch; lane 0's result is the tile granted.
         auto grab = [&](int32_t after) __attribute__((always_inline)) -> int32_t {
             if (p.deterministic) return after + NWAVES;
-            const int32_t t = __hip_atomic_fetch_add(&s_next_tile, lw == 0 ? 1 : 0,
+            const int32_t t = __hip_atomic_fetch_add(&s_tile_words[lw], lw == 0 ? 1 : 0,
                                                      __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
             return __builtin_amdgcn_readfirstlane(t);

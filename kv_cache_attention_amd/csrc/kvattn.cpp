@@ -105,8 +105,12 @@ int64_t max_attended(const kvattn_config& c, int q_len, int mask_mode, int n_sin
 // Element type of the caches (the config's kv_dtype, 0 meaning the same as dtype).
 int kv_dtype_of(const kvattn_config& c) { return c.kv_dtype == 0 ? c.dtype : c.kv_dtype; }
 
+// 16 to 64 rows per KV head (and more, in 64-row blocks, where the prefill kernel does
+// not apply): 16-bit caches of the query's type, or 8-bit E4M3 caches.
 bool use_mfma(const kvattn_config& c, int q_len) {
-    return kv_dtype_of(c) == c.dtype && kvattn::mfma_supported(c.dtype, c.head_dim, rows_of(c, q_len));
+    const int kv = kv_dtype_of(c);
+    return (kv == c.dtype || kv == KVATTN_FP8_E4M3) &&
+           kvattn::mfma_supported(c.dtype, c.head_dim, rows_of(c, q_len));
 }
 
 // Chunked prefill (more than 64 rows per KV head, contiguous or ring cache): the
@@ -220,7 +224,7 @@ int resident_for(const kvattn_config& c, int q_len, bool masked, int num_cus) {
     const bool prefill = use_prefill(c, q_len);
     const bool mfma = use_mfma(c, q_len);
     const void* k = prefill ? kvattn::select_prefill_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
-                    : mfma  ? kvattn::select_mfma_kernel(c.dtype, c.head_dim, rows, c.cache_mode)
+                    : mfma  ? kvattn::select_mfma_kernel(c.dtype, kv_dtype_of(c), c.head_dim, rows, c.cache_mode)
                             : kvattn::select_valu_kernel(c.dtype, kv_dtype_of(c), c.head_dim, rows,
                                                          c.cache_mode, masked);
     const int threads = prefill ? kvattn::kPrefillThreads
@@ -566,7 +570,8 @@ int launch_decode(kvattn_handle* h, const kvattn::DecodeParams& p, int grid, int
         use_prefill(h->cfg, q_len)
             ? kvattn::launch_prefill_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
         : use_mfma(h->cfg, q_len)
-            ? kvattn::launch_decode_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
+            ? kvattn::launch_decode_mfma(p, h->cfg.dtype, kv_dtype_of(h->cfg), h->cfg.head_dim,
+                                         grid, h->stream)
             : kvattn::launch_decode_valu(p, h->cfg.dtype, kv_dtype_of(h->cfg), h->cfg.head_dim,
                                          grid, h->stream);
     if (e != hipSuccess)

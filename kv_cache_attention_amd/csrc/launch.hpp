@@ -21,12 +21,13 @@ int valu_threads(int rows);  // workgroup size of the instance serving `rows`
 const void* select_valu_kernel(int dtype, int kv_dtype, int head_dim, int rows, int cache_mode,
                                bool masked);
 
-// Matrix-core split-KV kernel for 16 to 64 rows per KV head (f16 / bf16).
-hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,
-                              hipStream_t st);
+// Matrix-core split-KV kernel for 16 to 64 rows per KV head (f16 / bf16 queries;
+// caches of the same type or 8-bit E4M3 codes).
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int kv_dtype, int head_dim,
+                              int grid, hipStream_t st);
 bool mfma_supported(int dtype, int head_dim, int rows);
 int mfma_rows_per_block(int rows);  // rows of one segment (whole 16-row tiles, at most 64)
-const void* select_mfma_kernel(int dtype, int head_dim, int rows, int cache_mode);
+const void* select_mfma_kernel(int dtype, int kv_dtype, int head_dim, int rows, int cache_mode);
 constexpr int kMfmaThreads = 256;
 
 // Matrix-core kernel for chunked prefill: more than 64 rows per KV head (f16 / bf16,

@@ -116,6 +116,8 @@ PAGED_100K = Case("paged_100k", seed=5, batch=2, num_q_heads=32, num_kv_heads=8,
 DECODE_7B_FP8 = DECODE_7B.replace(name="decode_7b_fp8", seed=6, kv_dtype="fp8")
 SINK_WINDOW_FP8 = SINK_WINDOW.replace(name="sink_window_fp8", seed=7, kv_dtype="fp8")
 PAGED_100K_FP8 = PAGED_100K.replace(name="paged_100k_fp8", seed=8, kv_dtype="fp8")
+# speculative verification (40 rows per KV head: the matrix-core path) with an 8-bit cache
+SPEC_VERIFY_FP8 = SPEC_VERIFY.replace(name="spec_verify_fp8", seed=11, kv_dtype="fp8")
 
 # Token-tree verification: the verify step with 8 draft tokens per sequence arranged
 # as a seeded random tree (8 x GQA 8 = 64 rows per KV head).
@@ -128,8 +130,8 @@ CHUNKED_PREFILL = Case("chunked_prefill", seed=10, batch=4, num_q_heads=32, num_
                        q_len=512, seq_lens=(8192,) * 4, value_scale=0.5)
 
 CONFIGS = {c.name: c for c in (TINY, DECODE_7B, SPEC_VERIFY, SINK_WINDOW, PAGED_100K,
-                               DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8, TREE_VERIFY,
-                               CHUNKED_PREFILL)}
+                               DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8, SPEC_VERIFY_FP8,
+                               TREE_VERIFY, CHUNKED_PREFILL)}
 
 
 def tree_words_from_parents(parents) -> list:
@@ -312,9 +314,12 @@ def small_tree_variants():
 
 def small_fp8_variants():
     """Reduced cases with an 8-bit K/V cache: the reduced decode, ring and paged cases,
-    and a paged case with q_len 5 (per-row causal masks, 20 rows per KV head)."""
+    a paged case with q_len 5 (per-row causal masks, 20 rows per KV head) and the
+    reduced verify case (40 rows per KV head); the last two take the matrix cores."""
     sv = small_variants()
     return {
+        "spec_verify_small_fp8": sv["spec_verify_small"].replace(name="spec_verify_small_fp8",
+                                                                 kv_dtype="fp8", seed=27),
         "decode_7b_small_fp8": sv["decode_7b_small"].replace(name="decode_7b_small_fp8",
                                                              kv_dtype="fp8", seed=22),
         "sink_window_small_fp8": sv["sink_window_small"].replace(name="sink_window_small_fp8",

@@ -45,7 +45,7 @@ def test_fp8_sharp_softmax_matches_oracle(name):
     gh.check(out, ref, case.dtype, f"{name}/sharp")
 
 
-@pytest.mark.parametrize("name", ["decode_7b_small_fp8", "paged_small_q5_fp8"])
+@pytest.mark.parametrize("name", ["decode_7b_small_fp8", "paged_small_q5_fp8", "spec_verify_small_fp8"])
 @pytest.mark.parametrize("split_len", [64, 192])
 def test_fp8_unit_length_does_not_change_the_result(name, split_len):
     case = FP8[name]
