@@ -14,7 +14,10 @@ Prints ONE JSON line:
   roofline        the decode kernel timed with HIP events on the library's stream,
                   against MI355X's 8 TB/s HBM3E peak
   other_workloads the other workloads of the 70 %-of-peak target (decode_7b,
-                  spec_verify, sink_window), timed the same way in the same run
+                  spec_verify, sink_window), timed the same way in the same run, and
+                  decode_7b / spec_verify with the KV append fused in
+                  (kvattn_append_decode, "+append": one launch writes the new rows
+                  and attends; bytes add the new rows read and written)
   ceiling_gbs     a plain streaming read of 256 MiB and 1 GiB (the library's
                   yardstick kernel): the read bandwidth this device reaches in practice
   cpu_baseline    the oracle (test infrastructure) timed on the host cores over a
@@ -43,6 +46,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNELS = ["valu", "mfma", "prefill_mfma"]
 # the other workloads of the 70 %-of-peak target (the default line is the largest)
 OTHERS = ("decode_7b", "spec_verify", "sink_window")
+# the same steps with the KV append fused in (one launch: write the new rows, attend)
+APPEND_OTHERS = ("decode_7b+append", "spec_verify+append")
 DEVICE_WARMUP_MS = 100  # plain streaming reads before the warmup steps (clock ramp)
 
 
@@ -81,7 +86,7 @@ def parse():
     ap.add_argument("--layout", default="head_major", choices=["token_major", "head_major"])
     ap.add_argument("--split-len", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="K/V copies rotated (0 = auto)")
-    ap.add_argument("--others", default=",".join(OTHERS),
+    ap.add_argument("--others", default=",".join(OTHERS + APPEND_OTHERS),
                     help="further workloads timed in the same run ('' = none)")
     ap.add_argument("--other-steps", type=int, default=100)
     ap.add_argument("--no-ceiling", action="store_true")
@@ -140,12 +145,23 @@ class Workload:
     """One workload resident on the device, with rotated K/V copies and a handle bound
     to its own stream."""
 
-    def __init__(self, case, layout, split_len=0, copies=0, dev=None):
+    def __init__(self, case, layout, split_len=0, copies=0, dev=None, append=False):
         self.case = case
         d = workloads.make_inputs(case, device="cuda")
         self.d = d
         sl_host = d["seq_lens"].cpu().tolist()
         self.step_bytes = accounting.step_bytes(case, sl_host)
+        # append fused into the step (kvattn_append_decode): the q_len new K and V rows
+        # per sequence and KV head are read from k_new / v_new and written to the cache
+        self.append = append
+        if append:
+            g = torch.Generator().manual_seed(case.seed + 1000)
+            shape = (case.batch, case.q_len, case.num_kv_heads, case.head_dim)
+            dt = kb.TORCH_DTYPE[case.kv_dtype or case.dtype]
+            assert dt != torch.uint8, "fused-append workloads use 16-bit or 32-bit caches"
+            self.k_new = torch.randn(shape, generator=g).to(dt).to(d["q"].device)
+            self.v_new = torch.randn(shape, generator=g).to(dt).to(d["q"].device)
+            self.step_bytes += 2 * 2 * self.k_new.numel() * self.k_new.element_size()
         self.step_flops = accounting.step_flops(case, sl_host)
         # multiply-adds the rows really do (row by row; the union count above is an upper
         # bound): decides whether the step is bound by the matrix cores or by HBM
@@ -179,7 +195,11 @@ class Workload:
     def step(self, c, out=None):
         case, d = self.case, self.d
         out = self.out if out is None else out
-        if case.mask_mode == "tree":
+        if self.append:
+            kb.kvattn_append_decode(self.h.h, d["q"], self.k_new, self.v_new, self.kcs[c],
+                                    self.vcs[c], d["block_table"], d["seq_lens"], case.q_len,
+                                    self.mask, case.n_sink, case.window, out)
+        elif case.mask_mode == "tree":
             kb.kvattn_decode_tree(self.h.h, d["q"], self.kcs[c], self.vcs[c], d["block_table"],
                                   d["seq_lens"], case.q_len, d["tree_mask"], out)
         else:
@@ -354,7 +374,8 @@ def main():
     # the other workloads of the 70 %-of-peak target, timed the same way in the same run
     others = {}
     for name in [n for n in a.others.split(",") if n and n != case.name]:
-        o = Workload(workloads.CONFIGS[name], a.layout, 0, 0, dev)
+        base, _, suffix = name.partition("+")  # "<workload>+append": kvattn_append_decode
+        o = Workload(workloads.CONFIGS[base], a.layout, 0, 0, dev, append=suffix == "append")
         ot = o.time(a.other_steps, a.warmup)
         ach = o.step_bytes / (ot["launch_ms"] * 1e-3) / 1e9
         others[name] = {"us_per_step": round(ot["ms_per_step"] * 1e3, 2),

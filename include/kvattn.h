@@ -191,9 +191,15 @@ KVATTN_API int kvattn_append(kvattn_handle* h, const void* k_new, const void* v_
                              void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                              int32_t q_len, int32_t n_sink);
 
-/* kvattn_append followed by kvattn_decode on the same stream (two launches, in that
- * order): the decode sees the rows just written.  Arguments as for the two calls;
- * a RING cache uses n_sink for both (with KVATTN_MASK_SINK_WINDOW). */
+/* kvattn_append and kvattn_decode in one launch: the step writes the new tokens'
+ * keys and values back to the cache and attends over them (dothoosh.com
+ * speculative-decoding article, "The memory-bandwidth wall").  The result and the
+ * caches afterwards are those of kvattn_append followed by kvattn_decode: each
+ * workgroup writes the new rows that its share of the step reads before loading it
+ * (the new positions are the last of every attended list, and no attended position
+ * shares a slot with a new one), so no step-wide ordering is needed.  Arguments as
+ * for the two calls; a RING cache uses n_sink for both (with
+ * KVATTN_MASK_SINK_WINDOW).  k_new / v_new must not overlap the caches. */
 KVATTN_API int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new,
                                     const void* v_new, void* k_cache, void* v_cache,
                                     const int32_t* block_table, const int32_t* seq_lens,

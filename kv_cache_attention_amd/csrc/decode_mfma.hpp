@@ -37,6 +37,7 @@
 #include "mfma_common.hpp"
 #include "split_merge.hpp"
 #include "work_plan.hpp"
+#include "fused_append.hpp"
 
 namespace kvattn {
 // Workgroups per CU the register budget is cut for (row tiles <= 3).
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     const int lq = l / 16;  // operand k-group / output row group
 
     for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    if (p.k_new) append_unit_rows<CACHE, D, Elem<KT>::bytes, MFMA_THREADS>(p, fp, ui);
     for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
     const int b = pc.b;
     // more rows than one block holds (chunked prefill: hundreds of new rows) are cut

@@ -35,6 +35,7 @@
 #include "launch.hpp"
 #include "split_merge.hpp"
 #include "work_plan.hpp"
+#include "fused_append.hpp"
 
 namespace kvattn {
 
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
     };
 
     for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    if (p.k_new) append_unit_rows<CACHE, D, EB, THREADS>(p, fp, ui);
     // The next piece's Q rows and first wave tile are loaded before the current
     // piece's epilogue (merge across waves, stores, arrival), so they are in flight
     // while it runs.

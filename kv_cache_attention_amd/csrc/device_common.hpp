@@ -42,6 +42,11 @@ struct DecodeParams {
     const float* k_scale; // 8-bit caches: [Hkv] dequantisation scales (else NULL)
     const float* v_scale;
     const uint64_t* tree_mask;  // MASK_TREE: [batch, q_len] words, bit j = attends new position j
+    // Append fused into the decode: [batch, q_len, Hkv, D] rows of the cache's element
+    // type for positions T - q_len .. T - 1, written to their slots by the workgroups
+    // that read them (NULL: the caches already hold them)
+    const char* k_new;
+    const char* v_new;
     float scale_log2;     // softmax scale * log2(e): scores are kept in the exp2 domain
 };
 

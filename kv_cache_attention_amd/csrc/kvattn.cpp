@@ -528,6 +528,8 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.k_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->k_scale : nullptr;
     p.v_scale = kv_dtype_of(c) == KVATTN_FP8_E4M3 ? h->v_scale : nullptr;
     p.tree_mask = mask_mode == KVATTN_MASK_TREE ? tree : nullptr;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
     const float scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
     p.scale_log2 = scale * 1.4426950408889634f;
 }
@@ -710,13 +712,11 @@ int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new, con
     rc = prepare_append(h, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_len,
                         mask_mode == KVATTN_MASK_SINK_WINDOW ? n_sink : 0, &a);
     if (rc) return rc;
-    if ((a.n_chunks > 0 || grid > 0) &&
-        (rc = maybe_validate(h, block_table, seq_lens, q_len, nullptr)))
-        return rc;
-    if (a.n_chunks > 0) {
-        rc = launch_append(h, a);
-        if (rc) return rc;
-    }
+    if (grid == 0) return KVATTN_OK;  // no sequence holds a position: nothing to write
+    if ((rc = maybe_validate(h, block_table, seq_lens, q_len, nullptr))) return rc;
+    // one launch: the decode's workgroups write the new rows they read
+    p.k_new = static_cast<const char*>(k_new);
+    p.v_new = static_cast<const char*>(v_new);
     return launch_decode(h, p, grid, q_len);
 }
 

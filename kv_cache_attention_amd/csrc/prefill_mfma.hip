@@ -23,6 +23,7 @@
 #include "mfma_common.hpp"
 #include "split_merge.hpp"
 #include "work_plan.hpp"
+#include "fused_append.hpp"
 
 namespace kvattn {
 
@@ -67,6 +68,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
     const float c = p.scale_log2;
 
     for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    if (p.k_new) append_unit_rows<CACHE, D, 2, PF_THREADS>(p, fp, ui);
     for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
     const int b = pc.b;
     const int kvh = pc.seg / p.row_blocks;

@@ -1,8 +1,11 @@
 """GPU parity of the KV append (kvattn_append, kvattn_append_decode) through the C ABI:
 the caches after the append equal the oracle's append byte for byte (every element
-type, both layouts, the three cache forms, q_len 1..5, sequences shorter than the
-new block, ring wrap-around), the fused call's output matches the oracle's decode of
-the oracle-appended caches, and equals the two calls made separately bit for bit."""
+type, both layouts, the three cache forms, q_len 1..100, sequences shorter than the
+new block, ring wrap-around).  The fused call (one launch whose workgroups write the
+new rows they read) leaves the same cache bytes, its output matches the oracle's
+decode of the oracle-appended caches, and in deterministic mode equals the two calls
+made separately bit for bit, on all three kernel families (vector-ALU, split-KV
+matrix-core with one and with several row blocks per KV head, prefill)."""
 import pytest
 import torch
 
@@ -14,7 +17,7 @@ from tests import gpu_helpers as gh
 pytestmark = pytest.mark.gpu
 
 _S = workloads.small_variants()
-CASES = {**_S, **workloads.small_fp8_variants()}
+CASES = {**_S, **workloads.small_fp8_variants(), **workloads.small_prefill_variants()}
 # a sequence shorter than its block of new rows (no slot for its first rows)
 CASES["spec_verify_short"] = _S["spec_verify_small"].replace(name="spec_verify_short",
                                                              seq_lens=(1000, 3, 5))
@@ -72,8 +75,12 @@ def test_append_writes_the_oracles_slots(name, layout):
     assert torch.equal(_bytes(vc.cpu()), _bytes(ev)), "v_cache"
 
 
-@pytest.mark.parametrize("name", ["decode_7b_small", "spec_verify_short", "sink_window_q3",
-                                  "paged_small", "paged_small_q5_fp8", "tiny"])
+FUSED = ["decode_7b_small", "spec_verify_short", "sink_window_q3", "paged_small",
+         "paged_small_q5_fp8", "tiny", "spec_verify_small", "spec_verify_small_fp8",
+         "prefill_small", "prefill_paged", "prefill_ring", "prefill_d64"]
+
+
+@pytest.mark.parametrize("name", FUSED)
 def test_append_decode_matches_oracle_and_the_two_calls(name):
     case = CASES[name]
     print(f"append_decode case={name}", flush=True)
@@ -102,8 +109,42 @@ def test_append_decode_matches_oracle_and_the_two_calls(name):
                            case.mask_mode, case.n_sink, case.window)
         torch.cuda.synchronize()
         outs.append(out.cpu())
+        kc, vc = _from_head_major(case, kc), _from_head_major(case, vc)
+        assert torch.equal(_bytes(kc.cpu()), _bytes(ek)), f"k_cache (fused={fused})"
+        assert torch.equal(_bytes(vc.cpu()), _bytes(ev)), f"v_cache (fused={fused})"
     gh.check(outs[0], ref, case.dtype, name)
     assert torch.equal(outs[0], outs[1]), "fused call differs from append then decode"
+
+
+@pytest.mark.parametrize("name", ["decode_7b_small", "sink_window_q3", "paged_small",
+                                  "spec_verify_small", "prefill_small", "prefill_paged"])
+def test_fused_append_decode_token_major_shared_queue(name):
+    """The default (shared work queue) mode, token-major caches, two steps in a row:
+    the second step appends the next rows of the sequences the first one grew."""
+    case = CASES[name]
+    print(f"append_decode token-major case={name}", flush=True)
+    inp = workloads.make_inputs(case)
+    n_sink = case.n_sink if case.mask_mode == "sink_window" else 0
+    d = gh.to_device(inp)
+    kc, vc = d["k_cache"], d["v_cache"]
+    ek, ev = inp["k_cache"], inp["v_cache"]
+    h = _handle(case, "token_major")
+    lens = inp["seq_lens"].clone()
+    for step in range(2):
+        kn, vn = _new_rows(case, seed=21 + step)
+        ek, ev = oracle.append_np(case, ek, ev, kn, vn, inp["block_table"], lens, n_sink)
+        ref = oracle.decode(case, inp["q"], ek, ev, inp["block_table"], lens,
+                            k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+        out = h.append_decode(d["q"], kn.cuda(), vn.cuda(), kc, vc, d["block_table"],
+                              lens.cuda(), case.q_len, case.mask_mode, case.n_sink, case.window)
+        torch.cuda.synchronize()
+        gh.check(out.cpu(), ref, case.dtype, f"{name}/step{step}")
+        assert torch.equal(_bytes(kc.cpu()), _bytes(ek)), f"k_cache step {step}"
+        assert torch.equal(_bytes(vc.cpu()), _bytes(ev)), f"v_cache step {step}"
+        # the next step's lengths (contiguous and paged caches hold at most capacity)
+        lens = lens + case.q_len
+        if case.cache_mode != "ring":
+            lens = torch.clamp(lens, max=case.capacity)
 
 
 def test_append_skips_page_entries_outside_the_pool():
