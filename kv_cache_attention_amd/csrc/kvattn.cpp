@@ -113,7 +113,7 @@ bool use_mfma(const kvattn_config& c, int q_len) {
            kvattn::mfma_supported(c.dtype, c.head_dim, rows_of(c, q_len));
 }
 
-// Chunked prefill (more than 64 rows per KV head, contiguous or ring cache): the
+// Chunked prefill (more than 64 rows per KV head, 16-bit caches of every form): the
 // prefill kernel's 256-row blocks.
 bool use_prefill(const kvattn_config& c, int q_len) {
     return kv_dtype_of(c) == c.dtype &&

@@ -31,7 +31,7 @@ const void* select_mfma_kernel(int dtype, int kv_dtype, int head_dim, int rows, 
 constexpr int kMfmaThreads = 256;
 
 // Matrix-core kernel for chunked prefill: more than 64 rows per KV head (f16 / bf16,
-// contiguous and ring caches) in blocks of kPrefillRows rows, one segment each.
+// every cache form) in blocks of kPrefillRows rows, one segment each.
 hipError_t launch_prefill_mfma(const DecodeParams& p, int dtype, int head_dim, int grid,
                                hipStream_t st);
 bool prefill_supported(int dtype, int head_dim, int rows, int cache_mode);

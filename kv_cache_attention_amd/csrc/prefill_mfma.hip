@@ -16,8 +16,10 @@
 //    bytes: the 16 positions one read touches fall on distinct banks), the running
 //    (max, sum) per row, O^T += V^T . P^T with V^T read back with the gfx950
 //    transposed LDS read, as in the split-KV kernel.
-// Contiguous and ring caches; causal, sink/window and token-tree masks.  A segment's
-// pieces and their merge are the split-KV kernel's (split_merge.hpp).
+// Contiguous, ring and paged caches (a paged position behind a page-table entry
+// outside the pool is staged as a zero V row and a masked score: skipped); causal,
+// sink/window and token-tree masks.  A segment's pieces and their merge are the
+// split-KV kernel's (split_merge.hpp).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -51,6 +53,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
     constexpr int NB = 2;  // LDS tile buffers
     __shared__ __attribute__((aligned(16))) char kbuf[NB][TILE * KROW];
     __shared__ __attribute__((aligned(16))) char vbuf[NB][TILE * VROW];
+    // paged caches: 1 where the tile's position has its page in the pool, else 0
+    __shared__ __attribute__((aligned(16))) uint8_t in_pool[CACHE == PAGED ? NB : 1][TILE];
     constexpr int MROWS = 64;  // rows the merge takes at a time (bounds its registers)
     __shared__ MergeSmem<MROWS, PF_THREADS> msm;
 
@@ -117,27 +121,44 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
     // cc / CPR (within the kind), 16 bytes cc % CPR of its row.  Positions past the
     // piece read its last position (in bounds; their scores are masked), so loads of
     // tiles past the last one are harmless and need no branch.
-    u32x4 stg[PF_AHEAD][NCH];  // staging registers: tile t sits in slot t % PF_AHEAD
-    auto load_tile = [&](int32_t t, u32x4 (&stage)[NCH]) __attribute__((always_inline)) {
+    // A paged position whose page-table entry lies outside the pool reads block 0 (in
+    // bounds) and is flagged: its V chunks are staged as zeros, its in_pool byte as 0.
+    struct Stage {
+        u32x4 w[NCH];
+        uint32_t ok;  // paged: bit k set when chunk k's page is in the pool
+    };
+    Stage stg[PF_AHEAD];  // staging registers: tile t sits in slot t % PF_AHEAD
+    auto load_tile = [&](int32_t t, Stage& stage) __attribute__((always_inline)) {
+        stage.ok = 0;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int cc = tid + k * PF_THREADS;
             const int kind = cc / TCH;
             const int rem = cc - kind * TCH;
             const int32_t j = min(j0 + t * TILE + rem / CPR, j1 - 1);
-            const Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
+            Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
+            if constexpr (CACHE == PAGED) {
+                stage.ok |= (L.unit >= 0 ? 1u : 0u) << k;
+                L.unit = L.unit >= 0 ? L.unit : 0;
+            }
             const int64_t off = row_offset(p, L, kvh) + (rem % CPR) * 8;
-            stage[k] = *reinterpret_cast<const u32x4*>((kind ? vp : kp) + off);
+            stage.w[k] = *reinterpret_cast<const u32x4*>((kind ? vp : kp) + off);
         }
     };
-    auto store_tile = [&](int buf, const u32x4 (&stage)[NCH]) __attribute__((always_inline)) {
+    auto store_tile = [&](int buf, const Stage& stage) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int cc = tid + k * PF_THREADS;
             const int kind = cc / TCH;
             const int rem = cc - kind * TCH;
             char* dst = kind ? vbuf[buf] + (rem / CPR) * VROW : kbuf[buf] + (rem / CPR) * KROW;
-            *reinterpret_cast<u32x4*>(dst + (rem % CPR) * 16) = stage[k];
+            u32x4 w = stage.w[k];
+            if constexpr (CACHE == PAGED) {
+                const bool ok = (stage.ok >> k) & 1u;
+                if (kind && !ok) w = u32x4{0, 0, 0, 0};
+                if (!kind && rem % CPR == 0) in_pool[buf][rem / CPR] = ok ? 1 : 0;
+            }
+            *reinterpret_cast<u32x4*>(dst + (rem % CPR) * 16) = w;
         }
     };
 
@@ -163,8 +184,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
         store_tile(0, stg[0]);
     }
     __syncthreads();
-    auto tile = [&](int32_t t, u32x4 (&mine)[NCH], const u32x4 (&next)[NCH])
-                    __attribute__((always_inline)) {
+    auto tile = [&](int32_t t, Stage& mine, const Stage& next) __attribute__((always_inline)) {
         const int cur = t % NB;
         load_tile(t + PF_AHEAD, mine);
         const int32_t tb = j0 + t * TILE;
@@ -188,9 +208,17 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
         }
 
         // mask where it can bite: a partial tile, rows that do not all see the tile's
-        // last position, or the window mask
+        // last position, the window mask, or (paged) a position whose page is not in
+        // the pool; the lane's positions tt * 16 + lq * 4 + e have their in_pool
+        // bytes in one word per tt
+        uint32_t pool_w[2] = {0x01010101u, 0x01010101u};
+        if constexpr (CACHE == PAGED) {
+            pool_w[0] = *reinterpret_cast<const uint32_t*>(&in_pool[cur][lq * 4]);
+            pool_w[1] = *reinterpret_cast<const uint32_t*>(&in_pool[cur][16 + lq * 4]);
+        }
         const bool edge = (tb + TILE > j1) || sink_window ||
-                          span_pos(s, min(tb + TILE, j1) - 1) > hi_first;
+                          span_pos(s, min(tb + TILE, j1) - 1) > hi_first ||
+                          (CACHE == PAGED && __any((pool_w[0] & pool_w[1]) != 0x01010101u));
         if (edge) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -200,9 +228,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
                     const int32_t pos = span_pos(s, min(j, j1 - 1));
                     const int32_t rel = pos - P0;
                     const uint64_t bit = rel >= 0 ? 1ull << (rel & 63) : 0ull;
+                    const bool pooled = (pool_w[tt] >> (8 * e)) & 1u;
 #pragma unroll
                     for (int qt = 0; qt < PF_RW; ++qt) {
-                        const bool ok = (j < j1) & (pos <= hi[qt]) &
+                        const bool ok = (j < j1) & pooled & (pos <= hi[qt]) &
                                         (!sink_window | (pos < p.n_sink) |
                                          (pos > hi[qt] - p.window)) &
                                         ((rel < 0) | ((tm[qt] & bit) != 0));
@@ -336,14 +365,16 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
 }
 
 bool prefill_supported(int dtype, int head_dim, int rows, int cache_mode) {
+    (void)cache_mode;  // every cache form
     return (dtype == F16 || dtype == BF16) && (head_dim == 64 || head_dim == 128) &&
-           rows > KVATTN_PF_MIN_ROWS && cache_mode != PAGED;
+           rows > KVATTN_PF_MIN_ROWS;
 }
 
 template <int DT, int D>
 static const void* prefill_kernel_c(int cache_mode) {
-    return cache_mode == RING ? reinterpret_cast<const void*>(&prefill_mfma_kernel<DT, D, RING>)
-                              : reinterpret_cast<const void*>(&prefill_mfma_kernel<DT, D, CONTIGUOUS>);
+    return cache_mode == RING    ? reinterpret_cast<const void*>(&prefill_mfma_kernel<DT, D, RING>)
+           : cache_mode == PAGED ? reinterpret_cast<const void*>(&prefill_mfma_kernel<DT, D, PAGED>)
+                                 : reinterpret_cast<const void*>(&prefill_mfma_kernel<DT, D, CONTIGUOUS>);
 }
 
 const void* select_prefill_kernel(int dtype, int head_dim, int rows, int cache_mode) {

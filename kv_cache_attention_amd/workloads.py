@@ -129,9 +129,14 @@ CHUNKED_PREFILL = Case("chunked_prefill", seed=10, batch=4, num_q_heads=32, num_
                        head_dim=128, dtype="bf16", cache_mode="contiguous", capacity=8192,
                        q_len=512, seq_lens=(8192,) * 4, value_scale=0.5)
 
+# The same chunk over a paged cache (16-token pages, the pool shuffled over the batch).
+CHUNKED_PREFILL_PAGED = CHUNKED_PREFILL.replace(name="chunked_prefill_paged", seed=12,
+                                                cache_mode="paged", block_size=16,
+                                                num_blocks=2048)
+
 CONFIGS = {c.name: c for c in (TINY, DECODE_7B, SPEC_VERIFY, SINK_WINDOW, PAGED_100K,
                                DECODE_7B_FP8, SINK_WINDOW_FP8, PAGED_100K_FP8, SPEC_VERIFY_FP8,
-                               TREE_VERIFY, CHUNKED_PREFILL)}
+                               TREE_VERIFY, CHUNKED_PREFILL, CHUNKED_PREFILL_PAGED)}
 
 
 def tree_words_from_parents(parents) -> list:

@@ -81,13 +81,14 @@ def test_q_zero_gives_mean_of_attended_values(name):
     gh.check(out, ref, case.dtype, f"{name}/q0")
 
 
-@pytest.mark.parametrize("q_len", [1, 5])
+@pytest.mark.parametrize("q_len", [1, 5, 80])
 def test_out_of_pool_page_entries_are_skipped(q_len):
     """Page-table entries outside [0, num_blocks) are skipped (their positions are
     dropped, nothing outside the pool is read).  With q = 0 every row is the mean of V
     over the attended positions whose pages are valid.  q_len 1 runs the vector-ALU
-    kernel, q_len 5 (20 rows per KV head) the matrix-core one; the bad pages sit
-    mid-sequence, at a sequence start and in a short sequence."""
+    kernel, q_len 5 (20 rows per KV head) the split-KV matrix-core one, q_len 80 (320
+    rows) the prefill kernel; the bad pages sit mid-sequence, at a sequence start and
+    in a short sequence."""
     case = SMALL["paged_small"].replace(q_len=q_len)
     print(f"case=paged_small q_len={q_len} out-of-pool entries", flush=True)
     inp = workloads.make_inputs(case)

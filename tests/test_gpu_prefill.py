@@ -1,10 +1,11 @@
 """GPU parity of chunked prefill (q_len in the hundreds: the prefill kernel's 256-row
-blocks for contiguous and ring caches, 64-row blocks of the split-KV matrix-core kernel
-for paged ones) through the C ABI against the oracle: reduced cases in both layouts with
+blocks for 16-bit caches of every form, 64-row blocks of the split-KV matrix-core kernel
+for 8-bit ones) through the C ABI against the oracle: reduced cases in both layouts with
 never-attended slots poisoned (contiguous, ring with the sink/window mask, paged, a
-sequence shorter than its chunk, head_dim 64), sharp softmax, forced unit lengths (blocks cut into many pieces),
-the first rows of a chunk equal to a decode of the shorter prefix, and chunks of the
-largest q_len (1024) on each kernel, with sequences shorter than their chunk."""
+sequence shorter than its chunk, head_dim 64), sharp softmax, forced unit lengths
+(blocks cut into many pieces), the first rows of a chunk equal to a decode of the
+shorter prefix, and chunks of the largest q_len (1024) on each kernel, with sequences
+shorter than their chunk."""
 import pytest
 import torch
 
@@ -18,15 +19,19 @@ pytestmark = pytest.mark.gpu
 PREFILL = workloads.small_prefill_variants()
 
 # q_len 1024 (the most a handle accepts): 4,096 rows per KV head on the prefill kernel
-# (16 blocks) and on the split-KV kernel (paged, 64 blocks), 1,024 on the vector-ALU
-# kernel (f32); one sequence in each is shorter than its chunk.
+# (16 blocks; contiguous and paged) and on the split-KV kernel (8-bit paged cache, 64
+# blocks), 1,024 on the vector-ALU kernel (f32); one sequence in each is shorter than
+# its chunk.
 _SV = workloads.small_variants()
 MAX_Q = {
     "prefill_max": (workloads.CHUNKED_PREFILL.replace(
         name="prefill_max", batch=2, num_q_heads=8, num_kv_heads=2, capacity=1536,
         q_len=1024, seq_lens=(1536, 1000), seed=45), 2),
     "prefill_max_paged": (_SV["paged_small"].replace(
-        name="prefill_max_paged", q_len=1024, seq_lens=(1600, 1377, 33), seed=46), 1),
+        name="prefill_max_paged", q_len=1024, seq_lens=(1600, 1377, 33), seed=46), 2),
+    "prefill_max_paged_fp8": (_SV["paged_small"].replace(
+        name="prefill_max_paged_fp8", kv_dtype="fp8", q_len=1024, seq_lens=(1600, 1377, 33),
+        seed=48), 1),
     "prefill_max_f32": (_SV["decode_7b_small"].replace(
         name="prefill_max_f32", dtype="f32", batch=2, capacity=1200, seq_len_range=None,
         seq_lens=(1200, 1100), q_len=1024, seed=47), 0),
@@ -39,7 +44,7 @@ def _prep(case, scale_q=1.0):
         inp["q"] = (inp["q"].float() * scale_q).to(inp["q"].dtype)
     gh.poison_unattended(case, inp)
     ref = oracle.decode(case, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
-                        inp["seq_lens"])
+                        inp["seq_lens"], k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     return inp, ref
 
 
@@ -50,7 +55,7 @@ def test_prefill_small_workloads_match_oracle(name, layout):
     print(f"prefill case={name} layout={layout}", flush=True)
     h = kb.KVAttn.for_case(case, layout=layout)
     kernel = h.plan(case.q_len, case.mask_mode, case.n_sink, case.window)[2]
-    assert kernel == (1 if case.cache_mode == "paged" else 2), "matrix-core kernel"
+    assert kernel == 2, "prefill kernel"
     inp, ref = _prep(case)
     out = gh.run(case, gh.to_device(inp), layout=layout, handle=h)
     gh.check(out, ref, case.dtype, f"{name}/{layout}")

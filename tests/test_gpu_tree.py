@@ -49,7 +49,7 @@ def test_tree_sharp_softmax_matches_oracle(name):
 
 # kernel codes of kvattn_plan: 0 vector ALU, 1 split-KV matrix core, 2 prefill
 KERNELS = {"tree_small": 1, "tree_small_q8": 1, "tree_short": 1, "tree_valu": 0,
-           "tree_paged": 1, "tree_wide": 2, "tree_q64": 2, "tree_wide_paged": 1}
+           "tree_paged": 1, "tree_wide": 2, "tree_q64": 2, "tree_wide_paged": 2}
 
 
 @pytest.mark.parametrize("name", list(TREES))
