@@ -94,15 +94,22 @@ struct PartialReader {
 // Shared memory the merge needs (floats).
 template <int NROWS, int THREADS>
 struct MergeSmem {
-    float M[NROWS];
-    float L[NROWS];
-    float4 red[THREADS];
+    float4 red[THREADS];     // split groups' accumulators ...
+    float2 red_ml[THREADS];  // ... and their running (max, sum)
 };
 
 // Merges the nvalid partials of rows row0 .. row0 + NROWS - 1 of KV head kvh
 // (rows roff .. of slots slot0 ..) into the output and puts the segment's counter
 // back to zero.  Called by every thread of the workgroup that drew the segment's
 // last ticket.
+//
+// One pass over the partials: each thread owns float4 chunks of (row, d) - split
+// groups share the threads left over - and folds the partials in as it reads them,
+// with the same rescaling identity:
+//     M' = max(M, m_k),  L' = L 2^(M - M') + l_k 2^(m_k - M'),  A' = A 2^(M - M') + acc_k 2^(m_k - M').
+// Every load of a step (US partials x the thread's chunks, accumulators and (max,
+// sum) words together) is issued before any is used, so a merge of up to US x split
+// groups partials costs one memory latency.
 template <int DT, int D, int NROWS, int THREADS>
 __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int kvh, int row0,
                                                int64_t unit, int64_t slot0, int nvalid,
@@ -113,62 +120,17 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
     const int NR = p.seg_rows;  // partial k of row r: index (slot0 + k) * NR + r
     const PartialReader rd(p);
 
-    // per row: M and L over the splits.  G lanes per row (aligned groups within a
-    // wave) each fold every G-th split, loads issued in batches, then the group
-    // combines its running (max, sum) pairs with shuffles.
-    constexpr int G0 = THREADS / NROWS >= 64 ? 64 : THREADS / NROWS;
-    constexpr int G = G0 >= 32 ? G0 : (G0 >= 16 ? 16 : (G0 >= 8 ? 8 : (G0 >= 4 ? 4 : (G0 >= 2 ? 2 : 1))));
-    static_assert(NROWS * G <= THREADS, "row groups");
-    {
-        const int r = tid / G, g = tid % G;
-        const bool act = r < NROWS && row0 + r < p.rows;
-        const int64_t part0 = act ? slot0 * NR + roff + r : 0;
-        float mx = NEG_INF, ls = 0.0f;
-        for (int sp0 = g; sp0 < nvalid; sp0 += 8 * G) {
-            float2 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int sp = sp0 + u * G;
-                v[u] = rd.ml2(part0 + (int64_t)(sp < nvalid ? sp : g) * NR);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (sp0 + u * G >= nvalid) continue;
-                const float mn = fmaxf(mx, v[u].x);
-                const float mu = mn == NEG_INF ? 0.0f : mn;
-                ls = ls * fast_exp2(mx - mu) + v[u].y * fast_exp2(v[u].x - mu);
-                mx = mn;
-            }
-        }
-#pragma unroll
-        for (int o = G / 2; o > 0; o >>= 1) {
-            const float mo = __shfl_xor(mx, o, 64);
-            const float lo = __shfl_xor(ls, o, 64);
-            const float mn = fmaxf(mx, mo);
-            const float mu = mn == NEG_INF ? 0.0f : mn;
-            ls = ls * fast_exp2(mx - mu) + lo * fast_exp2(mo - mu);
-            mx = mn;
-        }
-        if (act && g == 0) {
-            sm.M[r] = mx == NEG_INF ? 0.0f : mx;
-            sm.L[r] = ls;
-        }
-    }
-    __syncthreads();
-
-    // accumulators: float4 chunks of (row, d); split groups share the remaining threads.
-    // Every load of a step is issued before any is used (4 splits x EPT chunks), so
-    // the merge costs a few memory latencies, not one per split.
     constexpr int E4 = NROWS * D / 4;
     constexpr int SG = E4 >= THREADS ? 1 : THREADS / E4;
     constexpr int EPT = E4 >= THREADS ? (E4 + THREADS - 1) / THREADS : 1;
-    constexpr int US = 4;  // splits per step
+    constexpr int US = 4;  // partials per step
     static_assert(E4 >= THREADS || THREADS % E4 == 0, "shape");
+    static_assert(SG == 1 || EPT == 1, "split groups hold one chunk each");
     const int sg = E4 >= THREADS ? 0 : tid / E4;
     int e4[EPT], r[EPT];
     bool live[EPT];
     int64_t part0[EPT];
-    float mu[EPT];
+    float mx[EPT], ls[EPT];
     float4 a[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
@@ -178,12 +140,26 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
         r[k] = e4[k] / (D / 4);
         live[k] = in && row0 + r[k] < p.rows;
         part0[k] = live[k] ? slot0 * NR + roff + r[k] : 0;
-        mu[k] = live[k] ? sm.M[r[k]] : 0.0f;
+        mx[k] = NEG_INF;
+        ls[k] = 0.0f;
         a[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // folds (m, l, acc) into the thread's running (mx, ls, a)
+    auto fold = [&](int k, float m, float l, float4 v) __attribute__((always_inline)) {
+        const float mn = fmaxf(mx[k], m);
+        const float mu = mn == NEG_INF ? 0.0f : mn;
+        const float fa = fast_exp2(mx[k] - mu);  // 0 while nothing was folded in
+        const float fb = fast_exp2(m - mu);      // 0 for an empty piece
+        ls[k] = ls[k] * fa + l * fb;
+        a[k].x = a[k].x * fa + v.x * fb;
+        a[k].y = a[k].y * fa + v.y * fb;
+        a[k].z = a[k].z * fa + v.z * fb;
+        a[k].w = a[k].w * fa + v.w * fb;
+        mx[k] = mn;
+    };
     for (int sp0 = sg; sp0 < nvalid; sp0 += US * SG) {
         float4 v[US][EPT];
-        float w[US][EPT];
+        float2 w[US][EPT];
 #pragma unroll
         for (int u = 0; u < US; ++u) {
             const int sp = sp0 + u * SG;
@@ -192,40 +168,32 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
             for (int k = 0; k < EPT; ++k) {
                 const int64_t part = part0[k] + (int64_t)spc * NR;
                 v[u][k] = rd.acc4(part * D + (e4[k] % (D / 4)) * 4);
-                w[u][k] = rd.ml2(part).x;
+                w[u][k] = rd.ml2(part);
             }
         }
 #pragma unroll
         for (int u = 0; u < US; ++u) {
             const bool in = sp0 + u * SG < nvalid;
 #pragma unroll
-            for (int k = 0; k < EPT; ++k) {
-                const float f = in ? fast_exp2(w[u][k] - mu[k]) : 0.0f;
-                a[k].x += f * v[u][k].x;
-                a[k].y += f * v[u][k].y;
-                a[k].z += f * v[u][k].z;
-                a[k].w += f * v[u][k].w;
-            }
+            for (int k = 0; k < EPT; ++k)
+                fold(k, in ? w[u][k].x : NEG_INF, in ? w[u][k].y : 0.0f, v[u][k]);
         }
     }
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
         if constexpr (SG > 1) {
             sm.red[tid] = a[k];
+            sm.red_ml[tid] = float2{mx[k], ls[k]};
             __syncthreads();
             if (sg == 0) {
                 for (int g2 = 1; g2 < SG; ++g2) {
-                    const float4 o = sm.red[g2 * E4 + e4[k]];
-                    a[k].x += o.x;
-                    a[k].y += o.y;
-                    a[k].z += o.z;
-                    a[k].w += o.w;
+                    const float2 o = sm.red_ml[g2 * E4 + e4[k]];
+                    fold(k, o.x, o.y, sm.red[g2 * E4 + e4[k]]);
                 }
             }
         }
         if (sg == 0 && live[k]) {
-            const float L = sm.L[r[k]];
-            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            const float inv = ls[k] > 0.0f ? 1.0f / ls[k] : 0.0f;
             const int64_t o = row_id_of(p, b, kvh, row0 + r[k]) * D + (e4[k] % (D / 4)) * 4;
             store_elem<DT>(p.out, o, a[k].x * inv);
             store_elem<DT>(p.out, o + 1, a[k].y * inv);
