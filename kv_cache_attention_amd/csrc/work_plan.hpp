@@ -218,29 +218,34 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Flat
 }
 
 // Runs body(u) for every unit this workgroup takes.  Workgroup w starts with unit
-// w; further units come from a device-wide counter (one atomic per unit, issued a
-// unit ahead), so workgroups that the memory system serves faster take more.  In
-// deterministic mode workgroup w takes units w, w + grid, ...  The last workgroup
-// to leave puts the counter back to zero for the next call: every workgroup
-// counts itself out only after its final take, so no take can follow the reset.
+// w; when there are more units than workgroups, further units come from a
+// device-wide counter (one atomic per unit, issued a unit ahead), so workgroups that
+// the memory system serves faster take more.  In deterministic mode workgroup w takes
+// units w, w + grid, ...  The last workgroup to leave puts the counter back to zero
+// for the next call: every workgroup counts itself out only after its final take, so
+// no take can follow the reset.  With no more units than workgroups (the usual plan)
+// the counter is not touched at all: every workgroup hitting one address at launch
+// and again at exit serialises for microseconds, and the loads that follow an atomic
+// wait for it.
 template <typename F>
 __device__ __forceinline__ void for_each_unit(const DecodeParams& p, const FlatPlan& fp, int wg,
                                               int n_wg, F&& body) {
     __shared__ int64_t s_next_unit[2];  // by iteration parity: a slot is rewritten only
                                         // after a barrier that follows every read of it
+    const bool queued = !p.deterministic && fp.n_units > n_wg;
     int64_t u = wg;
     for (int it = 0; u < fp.n_units; ++it) {
         int64_t next = 0;
         if (threadIdx.x == 0)  // issued now, its result is waited for only after the unit
-            next = p.deterministic ? u + n_wg
-                                   : (int64_t)n_wg + __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED,
-                                                                            __HIP_MEMORY_SCOPE_AGENT);
+            next = !queued ? u + n_wg
+                           : (int64_t)n_wg + __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT);
         body(u);
         if (threadIdx.x == 0) s_next_unit[it & 1] = next;
         __syncthreads();
         u = s_next_unit[it & 1];
     }
-    if (threadIdx.x == 0 && !p.deterministic) {
+    if (threadIdx.x == 0 && queued) {
         if (__hip_atomic_fetch_add(p.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
             n_wg - 1) {
             __hip_atomic_store(p.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
