@@ -360,8 +360,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
     // while it runs.
     bool preloaded = false;
     QF qv[ROWS];
-    for_each_piece_ahead(p, fp, ui, [&](const Piece& pc, const SeqSpan& s, bool has_next,
-                                       const Piece& npc, const SeqSpan& ns) __attribute__((always_inline)) {
+    for_each_piece_ahead(p, fp, ui, [&](const Piece& pc, const SeqSpan& s,
+                                       auto&& next) __attribute__((always_inline)) {
         const Ctx x = make_ctx(pc, s);
         const int b = x.b, kvh = x.kvh, rb = x.rb;
         const int32_t n_tiles = x.n_tiles;
@@ -533,7 +533,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             tile(kwB, vwB, kwA, vwA);
         }
 
-        if (has_next) {
+        Piece npc;
+        SeqSpan ns;
+        if (next(npc, ns)) {
             first_loads(make_ctx(npc, ns), qv);
             preloaded = true;
         }

@@ -69,9 +69,9 @@ struct SeqSpan {
     int32_t ring0;      // ... and its offset within the rolling slots
 };
 
-__device__ __forceinline__ SeqSpan seq_span(const DecodeParams& p, int b) {
+// The span of a sequence whose length (as seq_lens holds it) is T.
+__device__ __forceinline__ SeqSpan seq_span_of(const DecodeParams& p, int32_t T) {
     SeqSpan s;
-    int32_t T = p.seq_lens[b];
     if (T < 0) T = 0;
     // Contiguous and paged caches cannot hold more than `capacity` positions.
     if (p.cache_mode != RING && T > p.capacity) T = p.capacity;
@@ -96,6 +96,10 @@ __device__ __forceinline__ SeqSpan seq_span(const DecodeParams& p, int b) {
     if (p.cache_mode == RING && p.n_sink < p.capacity)
         s.ring0 = (s.ring_pos0 - p.n_sink) % (p.capacity - p.n_sink);
     return s;
+}
+
+__device__ __forceinline__ SeqSpan seq_span(const DecodeParams& p, int b) {
+    return seq_span_of(p, p.seq_lens[b]);
 }
 
 // Logical position of work index j.

@@ -23,16 +23,21 @@
 // The slot count is bounded by units + segments.
 //
 // Nothing here needs the host to know the lengths: each workgroup reads seq_lens
-// (a scan over the batch) before its first K/V load.
+// (a scan over the batch) before its first K/V load, and keeps them in LDS (batches
+// of up to kLenCache sequences), so finding a unit's pieces costs no further memory
+// round trip before the loads.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace kvattn {
 
+constexpr int kLenCache = 1024;  // sequences whose lengths the plan keeps in LDS
+
 // Per-thread view of the flat range after the scan over the batch: thread t owns
 // sequences [b0, b0 + per) and their flat offsets [excl, excl + mine).
 struct FlatPlan {
+    const int32_t* lens;  // LDS copy of seq_lens (batch <= kLenCache), else NULL
     int64_t total;   // W
     int64_t big;     // positions per head unit
     int64_t n_big;   // head units: [u * big, (u + 1) * big) for u < n_big
@@ -43,18 +48,31 @@ struct FlatPlan {
     int64_t excl, mine;
 };
 
+// Quotient of non-negative 64-bit integers, by a 32-bit division when both fit (the
+// usual case: the full 64-bit division is a long instruction sequence, and the plan
+// and piece arithmetic runs before a workgroup's first load).
+__device__ __forceinline__ int64_t div_nn(int64_t a, int64_t b) {
+    if ((((uint64_t)a | (uint64_t)b) >> 32) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
+    return a / b;
+}
+
 // First flat index of unit u, and the unit holding flat index x (< total): the
 // units partition the range in order, so both are monotone.
 __device__ __forceinline__ int64_t unit_begin(const FlatPlan& f, int64_t u) {
     return u < f.n_big ? u * f.big : f.xb + (u - f.n_big) * f.small;
 }
 __device__ __forceinline__ int64_t unit_of(const FlatPlan& f, int64_t x) {
-    return x < f.xb ? x / f.big : f.n_big + (x - f.xb) / f.small;
+    return x < f.xb ? div_nn(x, f.big) : f.n_big + div_nn(x - f.xb, f.small);
+}
+
+// Span of sequence b, from the plan's LDS copy of the lengths when it has one.
+__device__ __forceinline__ SeqSpan plan_span(const DecodeParams& p, const FlatPlan& f, int b) {
+    return f.lens ? seq_span_of(p, f.lens[b]) : seq_span(p, b);
 }
 
 // Flat work of sequence b: attended positions x segments per sequence.
-__device__ __forceinline__ int64_t seq_work(const DecodeParams& p, int b) {
-    return (int64_t)seq_span(p, b).count * p.segs_per_seq;
+__device__ __forceinline__ int64_t seq_work(const DecodeParams& p, const FlatPlan& f, int b) {
+    return (int64_t)plan_span(p, f, b).count * p.segs_per_seq;
 }
 
 template <int THREADS>
@@ -62,13 +80,21 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     static_assert(THREADS % 64 == 0 && THREADS <= 1024, "whole waves");
     constexpr int NW = THREADS / 64;
     __shared__ int64_t s_part[NW];
+    __shared__ int32_t s_lens[kLenCache];
     const int tid = threadIdx.x;
     FlatPlan f;
+    f.lens = nullptr;  // read from seq_lens while the plan is made
     f.per = (p.batch + THREADS - 1) / THREADS;  // sequences per thread
     f.b0 = tid * f.per;
     int64_t mine = 0;
-    for (int k = 0; k < f.per; ++k)
-        if (f.b0 + k < p.batch) mine += seq_work(p, f.b0 + k);
+    for (int k = 0; k < f.per; ++k) {
+        const int b = f.b0 + k;
+        if (b < p.batch) {
+            const int32_t T = p.seq_lens[b];
+            if (p.batch <= kLenCache) s_lens[b] = T;
+            mine += (int64_t)seq_span_of(p, T).count * p.segs_per_seq;
+        }
+    }
     // inclusive scan over the wave, then across waves
     const int lane = tid & 63;
     int64_t inc = mine;
@@ -78,7 +104,8 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
         if (lane >= o) inc += y;
     }
     if (lane == 63) s_part[tid >> 6] = inc;
-    __syncthreads();
+    __syncthreads();  // s_part and s_lens are complete
+    f.lens = p.batch <= kLenCache ? s_lens : nullptr;
     int64_t before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -90,13 +117,13 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     f.mine = mine;
     f.total = total;
     const int64_t units = (int64_t)n_wg * p.units_per_wg;
-    int64_t usz = (total + units - 1) / units;
+    int64_t usz = div_nn(total + units - 1, units);
     if (usz < p.min_chunk) usz = p.min_chunk;
     usz = (usz + 15) & ~(int64_t)15;
     // uniform units of usz positions, unless the tail applies: every workgroup has
     // a head unit, and those (>= min_chunk) leave a tail to share
     f.big = usz;
-    f.n_big = (total + usz - 1) / usz;
+    f.n_big = div_nn(total + usz - 1, usz);
     f.xb = f.n_big * usz;
     f.small = usz;
     if (p.tail_pct > 0 && f.n_big >= units) {
@@ -105,7 +132,7 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
         if (units * big < total) {
             const int64_t rest = total - units * big;
             const int64_t tu = (int64_t)n_wg * p.tail_units;
-            int64_t small = (rest + tu - 1) / tu;
+            int64_t small = div_nn(rest + tu - 1, tu);
             if (small < p.min_chunk) small = p.min_chunk;
             f.big = big;
             f.n_big = units;
@@ -113,8 +140,8 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
             f.small = (small + 15) & ~(int64_t)15;
         }
     }
-    f.n_units = f.xb >= total ? (total + f.big - 1) / f.big
-                              : f.n_big + (total - f.xb + f.small - 1) / f.small;
+    f.n_units = f.xb >= total ? div_nn(total + f.big - 1, f.big)
+                              : f.n_big + div_nn(total - f.xb + f.small - 1, f.small);
     return f;
 }
 
@@ -132,7 +159,7 @@ __device__ __forceinline__ SeqAt seq_at(const DecodeParams& p, const FlatPlan& f
     if (f.excl <= x && x < f.excl + f.mine) {
         int64_t off = f.excl;
         for (int k = 0; k < f.per; ++k) {
-            const int64_t w = seq_work(p, f.b0 + k);
+            const int64_t w = seq_work(p, f, f.b0 + k);
             if (x < off + w) {
                 s_b = f.b0 + k;
                 s_off = off;
@@ -157,9 +184,11 @@ struct Piece {
     int part;       // this piece's index among them
 };
 
-// Calls f(piece, span, has_next, next_piece, next_span) for each piece of unit u,
-// in flat order; the next piece of the unit (if any) is known while the current
-// one runs, so its first loads can be issued before the current one's epilogue.
+// Calls f(piece, span, next) for each piece of unit u, in flat order.  next(np, ns)
+// (at most one call, in every thread or in none) gives the unit's next piece and
+// returns whether there is one, so a kernel can issue its first loads before the
+// current piece's epilogue; the next piece is worked out only then, after the
+// current piece's own first loads are in flight.
 template <typename F>
 __device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, const FlatPlan& fp,
                                                      int64_t u, F&& f) {
@@ -168,17 +197,17 @@ __device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, cons
     const SeqAt at = seq_at(p, fp, x0);
     int b = at.b;
     int64_t off_b = at.off;
-    SeqSpan sb = seq_span(p, b);
+    SeqSpan sb = plan_span(p, fp, b);
     // the piece that starts at flat index x (< x1)
     auto piece_at = [&](int64_t x, Piece& pc, SeqSpan& ps) __attribute__((always_inline)) {
         // sequences that hold nothing, or that x is already past, are skipped
         while (x >= off_b + (int64_t)sb.count * p.segs_per_seq) {
             off_b += (int64_t)sb.count * p.segs_per_seq;
             ++b;
-            sb = seq_span(p, b);
+            sb = plan_span(p, fp, b);
         }
         pc.b = b;
-        pc.seg = (int)((x - off_b) / sb.count);
+        pc.seg = (int)div_nn(x - off_b, sb.count);
         const int64_t seg0 = off_b + (int64_t)pc.seg * sb.count;
         pc.ja = (int32_t)(x - seg0);
         pc.jb = (int32_t)min<int64_t>(sb.count, x1 - seg0);
@@ -196,12 +225,21 @@ __device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, cons
     SeqSpan cs;
     int64_t x = piece_at(x0, cur, cs);
     for (;;) {
+        const bool more = x < x1;
+        bool known = false;
         Piece nx = cur;
         SeqSpan ns = cs;
-        const bool more = x < x1;
-        const int64_t xn = more ? piece_at(x, nx, ns) : x;
-        f(cur, cs, more, nx, ns);
+        int64_t xn = x;
+        auto next = [&](Piece& np, SeqSpan& nps) __attribute__((always_inline)) {
+            if (more && !known) xn = piece_at(x, nx, ns);
+            known = true;
+            np = nx;
+            nps = ns;
+            return more;
+        };
+        f(cur, cs, next);
         if (!more) break;
+        if (!known) xn = piece_at(x, nx, ns);
         cur = nx;
         cs = ns;
         x = xn;
@@ -213,8 +251,9 @@ template <typename F>
 __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const FlatPlan& fp,
                                                int64_t u, F&& f) {
     for_each_piece_ahead(p, fp, u,
-                         [&](const Piece& pc, const SeqSpan& s, bool, const Piece&,
-                             const SeqSpan&) __attribute__((always_inline)) { f(pc, s); });
+                         [&](const Piece& pc, const SeqSpan& s, auto&&) __attribute__((always_inline)) {
+                             f(pc, s);
+                         });
 }
 
 // Runs body(u) for every unit this workgroup takes.  Workgroup w starts with unit
