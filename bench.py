@@ -382,7 +382,13 @@ def main():
                         "launch_us": round(ot["launch_ms"] * 1e3, 2),
                         "bracketed_us_mean": round(ot["ev_mean_ms"] * 1e3, 2),
                         "bytes_per_step": o.step_bytes, "achieved_gbs": round(ach, 1),
-                        "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": KERNELS[o.plan[2]]}
+                        "bound": "hbm", "frac": round(ach / HBM_PEAK_GBS, 4),
+                        "kernel": KERNELS[o.plan[2]]}
+        if o.mfma_bound:  # the matrix cores bound this step: row flops against their peak
+            tf = o.row_flops / (ot["launch_ms"] * 1e-3) / 1e12
+            others[name].update({"bound": "mfma", "row_flops_per_step": o.row_flops,
+                                 "achieved_tflops": round(tf, 1),
+                                 "frac": round(tf / MFMA_PEAK_TFLOPS[o.case.dtype], 4)})
         o.close()
         del o
         torch.cuda.empty_cache()

@@ -6,8 +6,9 @@
 // ones of a sequence's attended list, and each is read only by the pieces that cover
 // it; every workgroup, before the first load of a unit, writes the new rows that the
 // unit's pieces read (K and V of the piece's KV head, from k_new / v_new) and waits
-// for the stores, so its own later loads see them.  Pieces of other row blocks of the
-// same (sequence, KV head) write the same rows again, with the same bytes.  No
+// until the stores are acknowledged, so its own later loads see them.  Pieces of
+// other row blocks of the same (sequence, KV head) write the same rows again, with
+// the same bytes.  No
 // attended position shares a slot with a new one (a ring keeps n_sink + window +
 // q_len - 1 <= capacity), so no other load of the step can see a slot change.  Rows
 // without a slot (position < 0, past a contiguous or paged cache's capacity, a
@@ -19,7 +20,8 @@
 namespace kvattn {
 
 // D: head_dim; EB: bytes per cache element (D * EB is a multiple of 16).  Every
-// thread of the workgroup calls it; it returns after a workgroup barrier.
+// thread of the workgroup calls it; it returns after a workgroup barrier that follows
+// the acknowledgement of every store.
 template <int CACHE, int D, int EB, int THREADS>
 __device__ __forceinline__ void append_unit_rows(const DecodeParams& p, const FlatPlan& fp,
                                                  int64_t u) {
@@ -53,8 +55,10 @@ __device__ __forceinline__ void append_unit_rows(const DecodeParams& p, const Fl
             *reinterpret_cast<uint4*>(vc + dst) = vx;
         }
     });
-    // the barrier orders the stores before every later load of the workgroup (its
-    // waves share one CU and its write-through L1)
+    // Every store is acknowledged (written to L2) before the barrier: a barrier alone
+    // orders the instructions, not their completion, and the streaming K/V loads that
+    // follow go to L2 and could reach it first.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 }
 
