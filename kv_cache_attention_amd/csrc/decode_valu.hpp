@@ -268,6 +268,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
         int32_t ja, jb, n_tiles;
         SeqSpan s;
         const char* kb;
+        const char* klast;  // contiguous and ring caches: the lane's K chunk of the piece's last row
     };
     auto make_ctx = [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
         Ctx x;
@@ -280,6 +281,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
         x.s = s;
         x.kb = reinterpret_cast<const char*>(p.k) + ((int64_t)x.kvh * p.stride_head + d0) * EB;
         if constexpr (CACHE != PAGED) x.kb += (int64_t)x.b * p.stride_seq * EB;
+        x.klast = x.kb;
+        if constexpr (CACHE != PAGED) {
+            const Loc L = locate<CACHE>(p, s, x.b, span_pos(s, pc.jb - 1));
+            x.klast = x.kb + (uint64_t)(uint32_t)L.idx * tok_bytes;
+        }
         return x;
     };
     // Query rows of a piece's KV head: row r = i * group + hg (new token i, head
@@ -461,10 +467,17 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             bool vok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) vok[u] = val[u];
-            // The next tile's loads are issued unconditionally (past the last tile they
-            // re-read this tile's valid addresses), which keeps the loop free of
-            // merges of loaded and not-loaded registers.
-            if (more) address(x, nxt);
+            // The next tile's loads are issued unconditionally, which keeps the loop
+            // free of merges of loaded and not-loaded registers.  Past the last tile
+            // (contiguous and ring caches) they all read the piece's last row, one row
+            // per load instruction: streaming loads leave nothing in L2 for a re-read of
+            // the whole tile to hit.
+            if (more) {
+                address(x, nxt);
+            } else if constexpr (CACHE != PAGED) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) ka[u] = x.klast;
+            }
             int32_t n2 = n_tiles;
             if constexpr (CACHE == PAGED) {
                 if (more) n2 = grab(nxt);
