@@ -469,14 +469,24 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
             for (int u = 0; u < U; ++u) vok[u] = val[u];
             // The next tile's loads are issued unconditionally, which keeps the loop
             // free of merges of loaded and not-loaded registers.  Past the last tile
-            // (contiguous and ring caches) they all read the piece's last row, one row
-            // per load instruction: streaming loads leave nothing in L2 for a re-read of
-            // the whole tile to hit.
+            // they read one row (contiguous and ring caches: the piece's last) per load
+            // instruction: streaming loads leave nothing in L2 for a re-read of the
+            // whole tile to hit.
             if (more) {
                 address(x, nxt);
             } else if constexpr (CACHE != PAGED) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) ka[u] = x.klast;
+            } else {
+                // paged: the row lane 0 read (a valid address), one chunk per instruction
+                // (readfirstlane returns a signed int: each half is widened through
+                // uint32_t, so a low half with bit 31 set does not sign-extend)
+                const uint64_t a0 = (uint64_t)ka[0];
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a0 >> 32));
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a0);
+                const uint64_t a = ((uint64_t)hi << 32) | (uint64_t)lo;
+#pragma unroll
+                for (int u = 0; u < U; ++u) ka[u] = reinterpret_cast<const char*>(a);
             }
             int32_t n2 = n_tiles;
             if constexpr (CACHE == PAGED) {
