@@ -118,26 +118,6 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     const int32_t j0 = pc.ja;
     const int32_t j1 = pc.jb;
 
-    // rows' new-token index (for the causal / window mask); padding rows act as the last
-    int row_i[R];
-#pragma unroll
-    for (int qt = 0; qt < R; ++qt) {
-        const int n = row0 + qt * 16 + lr;
-        row_i[qt] = n < p.rows ? n / p.group : p.q_len - 1;
-    }
-
-    f32x4 o[DT16][R];
-#pragma unroll
-    for (int dt = 0; dt < DT16; ++dt)
-#pragma unroll
-        for (int qt = 0; qt < R; ++qt) o[dt][qt] = f32x4{0, 0, 0, 0};
-    float m[R], lsum[R];
-#pragma unroll
-    for (int qt = 0; qt < R; ++qt) {
-        m[qt] = NEG_INF;
-        lsum[qt] = 0.0f;
-    }
-
     char* vbuf = smem + wave * G::VBUF;
     constexpr int EB = Elem<KT>::bytes;  // bytes per cache element
     const char* kp = reinterpret_cast<const char*>(p.k);
@@ -172,9 +152,39 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         }
     };
 
+    // The first tile's K and V go in flight before the rest of the piece's setup (row
+    // bounds, accumulators, Q): each wave's first load is then a few instructions
+    // after the piece is known.
+    const int32_t n_tiles = (j1 - j0 + TILE - 1) / TILE;
+    u32x4 kc[2][KS], vr[NV];
+    int32_t cur = wave;
+    if (cur < n_tiles) {
+        load_k(j0 + cur * TILE, kc);
+        load_v(j0 + cur * TILE, vr);
+    }
+
+    // rows' new-token index (for the causal / window mask); padding rows act as the last
+    int row_i[R];
+#pragma unroll
+    for (int qt = 0; qt < R; ++qt) {
+        const int n = row0 + qt * 16 + lr;
+        row_i[qt] = n < p.rows ? n / p.group : p.q_len - 1;
+    }
+
+    f32x4 o[DT16][R];
+#pragma unroll
+    for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < R; ++qt) o[dt][qt] = f32x4{0, 0, 0, 0};
+    float m[R], lsum[R];
+#pragma unroll
+    for (int qt = 0; qt < R; ++qt) {
+        m[qt] = NEG_INF;
+        lsum[qt] = 0.0f;
+    }
+
     // Q^T operand fragments (LDS): fragment f = qt*KS + ks; lane l holds row
-    // qt*16 + l%16, d chunk (ks*4 + l/16)*8.  Loaded first, stored after the first
-    // tile's loads are in flight.
+    // qt*16 + l%16, d chunk (ks*4 + l/16)*8.
     constexpr int QPT = (G::QFRAGS * 64 + MFMA_THREADS - 1) / MFMA_THREADS;
     u32x4 qreg[QPT];
 #pragma unroll
@@ -198,7 +208,6 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     // deterministic mode wave w takes tiles w, w + waves, ...  The next tile is
     // known one tile ahead, and the one after is requested at the top of each
     // iteration, so the LDS atomic's latency is not waited for.
-    const int32_t n_tiles = (j1 - j0 + TILE - 1) / TILE;
     if (tid == 0) s_next_tile = MFMA_WAVES;
     // Every lane takes part in the atomic (lane 0 adds 1 to the counter, lane l adds 0
     // to its own word l): no lane-divergent branch in the tile loop.
@@ -214,15 +223,8 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     // loads are issued unconditionally (past the last tile, positions clamp to the
     // piece's last one), so no path through the loop lacks them and the compiler's
     // waits stay partial: V staging waits for V only, S^T for K only.
-    u32x4 kc[2][KS], vr[NV];
-    int32_t cur = wave;
-    if (cur < n_tiles) {
-        load_k(j0 + cur * TILE, kc);
-        load_v(j0 + cur * TILE, vr);
-    }
-
-    // Q staged from registers once the loads above are issued (the Q loads were
-    // issued first, so waiting for them does not wait for the tile)
+    // Q staged from registers (the load counter is in order: this waits for the first
+    // tile's loads as well, which the loop's first step needs anyway)
 #pragma unroll
     for (int k = 0; k < QPT; ++k)
         if (tid + k * MFMA_THREADS < G::QFRAGS * 64) qsm[tid + k * MFMA_THREADS] = qreg[k];
