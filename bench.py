@@ -52,14 +52,18 @@ DEVICE_WARMUP_MS = 100  # plain streaming reads before the warmup steps (clock r
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: HBM traffic measured for other sources is not reported."""
+    """Hash of the HIP sources and of the build script (its compiler flags): HBM traffic
+    measured for other sources or flags is not reported."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "kv_cache_attention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    pkg = os.path.join(ROOT, "kv_cache_attention_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = [(name, os.path.join(csrc, name)) for name in sorted(os.listdir(csrc))
+             if name.endswith((".hip", ".hpp", ".cpp"))]
+    files.append(("build.py", os.path.join(pkg, "build.py")))
+    for name, path in files:
+        with open(path, "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

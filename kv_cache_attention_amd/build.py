@@ -35,11 +35,22 @@ FLAGS = [
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
 
+# Per-source additions.  The split-KV matrix-core kernels keep their output accumulators
+# in ordinary vector registers (the matrix instructions read and write them there):
+# with the accumulators in the accumulation registers, the rare rescale of the online
+# softmax, which needs vector arithmetic on them, led the register allocator to copy
+# all of them on every tile.
+MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {
+    "decode_mfma.hip": MFMA_VGPR,
+    "decode_mfma_fp8.hip": MFMA_VGPR,
+}
+
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *lang, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *lang, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
