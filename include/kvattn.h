@@ -162,6 +162,12 @@ KVATTN_API int kvattn_create(const kvattn_config* cfg, kvattn_handle** out);
  *                RING: n_sink + window + q_len - 1 <= capacity and n_sink < capacity
  *   out          [batch, q_len, Hq, D]           device, written
  * batch is the handle's current batch (kvattn_set_batch; initially max_batch).
+ * One kernel launch; several, one per batch range and in order on the stream, when
+ * batch x KV heads x query-row blocks x the longest attended set the arguments allow
+ * (capacity, or n_sink + window + q_len - 1 for SINK_WINDOW) exceeds 2^30 position
+ * units (the kernels index that range in 32 bits); KVATTN_ERR_CAPACITY if a single
+ * sequence exceeds it.  The environment variable KVATTN_MAX_FLAT, read when a handle
+ * is created, lowers the limit (tests of the batch-range launches).
  */
 KVATTN_API int kvattn_decode(kvattn_handle* h, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_table, const int32_t* seq_lens, int32_t q_len,

@@ -23,6 +23,8 @@ SOURCES = ["kvattn.cpp", "decode_valu.hip", "valu_f16.hip", "valu_bf16.hip", "va
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden", "-Wall",
+    # an oversized shift is undefined and lets the compiler drop the code after it
+    "-Werror=shift-count-overflow", "-Werror=shift-count-negative",
     # no packed fp32 arithmetic on the device (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # leave branches on wave-uniform conditions unstructured: the decode tile loops

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     const int lr = l % 16;  // operand row / output column
     const int lq = l / 16;  // operand k-group / output row group
 
-    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    for_each_unit(p, fp, wg, n_wg, [&](int32_t ui) __attribute__((always_inline)) {
     if (p.k_new) append_unit_rows<CACHE, D, Elem<KT>::bytes, MFMA_THREADS>(p, fp, ui);
     for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
     const int b = pc.b;
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             const uint2 w = {pack2<DT>(A.x * inv, A.y * inv), pack2<DT>(A.z * inv, A.w * inv)};
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
         } else {
-            const int64_t part = (pc.slot0 + pc.part) * NQ + n;
+            const int64_t part = (int64_t)(pc.slot0 + pc.part) * NQ + n;
             store_partial4(p, part * D + d, A);
             if (d == 0) store_partial_ml(p, part, M, L);
         }

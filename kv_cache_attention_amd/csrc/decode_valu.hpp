@@ -359,7 +359,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
         }
     };
 
-    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    for_each_unit(p, fp, wg, n_wg, [&](int32_t ui) __attribute__((always_inline)) {
     if (p.k_new) append_unit_rows<CACHE, D, EB, THREADS>(p, fp, ui);
     // The next piece's Q rows and first wave tile are loaded before the current
     // piece's epilogue (merge across waves, stores, arrival), so they are in flight
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
                 const int64_t rid = row_id_of(p, b, kvh, rb * ROWS + r);
                 store_elem<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
             } else {
-                const int64_t part = (pc.slot0 + pc.part) * ROWS + r;
+                const int64_t part = (int64_t)(pc.slot0 + pc.part) * ROWS + r;
                 store_partial(p.ws_acc + part * D + d, A);
                 if (d == 0) {
                     store_partial(p.ws_ml + part * 2, M);

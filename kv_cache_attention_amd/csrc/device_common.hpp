@@ -14,6 +14,11 @@ enum : int { CONTIGUOUS = 0, PAGED = 1, RING = 2 };
 enum : int { MASK_CAUSAL = 0, MASK_SINK_WINDOW = 1, MASK_TREE = 2 };
 
 // Everything a decode launch needs, passed by value as the kernel argument.
+// Largest flat range (position-units: attended positions x segments, summed over the
+// batch) of one launch; the host cuts a launch over batch ranges to stay within it, so
+// the plan's indices are 32-bit with room for a unit past the end.
+constexpr int32_t kFlatMax = 1 << 30;
+
 struct DecodeParams {
     const void* q;
     const void* k;
@@ -35,7 +40,8 @@ struct DecodeParams {
     int32_t segs_per_seq; // num_kv_heads * row_blocks
     int32_t seg_rows;     // rows per segment as laid out in the workspace
     int32_t min_chunk;    // smallest unit (positions)
-    int32_t units_per_wg; // units per workgroup the flat range is cut into
+    int32_t units_per_wg; // units per workgroup the flat range is cut into (0: units of
+                          // exactly min_chunk positions)
     int32_t tail_pct;     // share (percent) of the flat range left to a dynamic tail (0: none)
     int32_t tail_units;   // tail units per workgroup
     int32_t deterministic;  // waves take fixed tiles instead of a shared queue

@@ -24,7 +24,7 @@ namespace kvattn {
 // the acknowledgement of every store.
 template <int CACHE, int D, int EB, int THREADS>
 __device__ __forceinline__ void append_unit_rows(const DecodeParams& p, const FlatPlan& fp,
-                                                 int64_t u) {
+                                                 int32_t u) {
     constexpr int RB = D * EB;    // bytes per row
     constexpr int CPR = RB / 16;  // 16-byte chunks per row
     static_assert(RB % 16 == 0, "rows of whole 16-byte chunks");

@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 
@@ -74,6 +75,7 @@ struct kvattn_handle {
     hipStream_t stream;
     int32_t batch;
     int32_t forced_chunk;
+    int64_t flat_max;       // largest flat range of one launch (kvattn::kFlatMax)
     const float* k_scale;   // 8-bit caches: per-KV-head dequantisation scales (device)
     const float* v_scale;
     float* ws;              // partials: acc [ws_part_rows, D] (the handle's allocation starts here)
@@ -362,6 +364,13 @@ int init_handle(kvattn_handle* h, const kvattn_config* cfg) {
     h->stream = nullptr;
     h->batch = cfg->max_batch;
     h->forced_chunk = 0;
+    // KVATTN_MAX_FLAT lowers the per-launch flat range (tests of the batch-range split
+    // on small shapes); it cannot raise it
+    h->flat_max = kvattn::kFlatMax;
+    if (const char* e = std::getenv("KVATTN_MAX_FLAT")) {
+        const long long v = std::atoll(e);
+        if (v >= 1 && v < h->flat_max) h->flat_max = v;
+    }
     h->k_scale = nullptr;
     h->v_scale = nullptr;
     const int64_t D = cfg->head_dim, H = cfg->num_kv_heads;
@@ -465,8 +474,9 @@ int kvattn_set_kv_scales(kvattn_handle* h, const float* k_scale, const float* v_
 
 int kvattn_set_split_len(kvattn_handle* h, int32_t split_len) {
     if (!h) return fail(KVATTN_ERR_INVALID_ARG, "handle is NULL");
-    if (split_len < 0 || split_len % kChunkQuantum)
-        return fail(KVATTN_ERR_INVALID_ARG, "split_len must be 0 or a positive multiple of 64");
+    if (split_len < 0 || split_len % kChunkQuantum || split_len > (1 << 24))
+        return fail(KVATTN_ERR_INVALID_ARG,
+                    "split_len must be 0 or a positive multiple of 64 up to 2^24");
     h->forced_chunk = split_len;
     return KVATTN_OK;
 }
@@ -521,7 +531,7 @@ static void fill_params(const kvattn_handle* h, kvattn::DecodeParams& p, const v
     p.segs_per_seq = (int32_t)segs_per_seq_of(c, q_len);
     p.seg_rows = seg_rows_of(c, q_len);
     p.min_chunk = min_chunk;
-    p.units_per_wg = h->forced_chunk > 0 ? 1 << 30 : kUnitsPerWg;  // forced: units of exactly min_chunk
+    p.units_per_wg = h->forced_chunk > 0 ? 0 : kUnitsPerWg;  // 0: units of exactly min_chunk
     p.tail_pct = h->forced_chunk > 0 ? 0 : kTailPct;
     p.tail_units = kTailUnits;
     p.deterministic = (c.flags & KVATTN_FLAG_DETERMINISTIC) ? 1 : 0;
@@ -566,8 +576,34 @@ int prepare_decode(kvattn_handle* h, const void* q, const void* k_cache, const v
     return KVATTN_OK;
 }
 
-int launch_decode(kvattn_handle* h, const kvattn::DecodeParams& p, int grid, int32_t q_len) {
-    if (grid == 0) return KVATTN_OK;
+int dtype_bytes(int dtype) {
+    return dtype == KVATTN_F32 ? 4 : (dtype == KVATTN_FP8_E4M3 ? 1 : 2);
+}
+
+// Parameters of sequences b0 .. b0 + nb - 1 of a decode: the batch-indexed arguments
+// start at sequence b0 (caches of the contiguous and ring forms hold a region per
+// sequence; a paged pool is shared and its page table starts at row b0).
+void batch_range(const kvattn_handle* h, kvattn::DecodeParams& p, int32_t b0, int32_t nb) {
+    const kvattn_config& c = h->cfg;
+    const int64_t qrow = (int64_t)p.q_len * c.num_q_heads * c.head_dim * dtype_bytes(c.dtype);
+    const int64_t eb = dtype_bytes(kv_dtype_of(c));
+    p.q = static_cast<const char*>(p.q) + b0 * qrow;
+    p.out = static_cast<char*>(p.out) + b0 * qrow;
+    p.seq_lens += b0;
+    if (c.cache_mode == KVATTN_PAGED) {
+        p.block_table += (int64_t)b0 * p.blocks_per_seq;
+    } else {
+        p.k = static_cast<const char*>(p.k) + b0 * p.stride_seq * eb;
+        p.v = static_cast<const char*>(p.v) + b0 * p.stride_seq * eb;
+    }
+    if (p.tree_mask) p.tree_mask += (int64_t)b0 * p.q_len;
+    const int64_t nrow = (int64_t)p.q_len * c.num_kv_heads * c.head_dim * eb;
+    if (p.k_new) p.k_new += b0 * nrow;
+    if (p.v_new) p.v_new += b0 * nrow;
+    p.batch = nb;
+}
+
+int launch_range(kvattn_handle* h, const kvattn::DecodeParams& p, int grid, int32_t q_len) {
     hipError_t e =
         use_prefill(h->cfg, q_len)
             ? kvattn::launch_prefill_mfma(p, h->cfg.dtype, h->cfg.head_dim, grid, h->stream)
@@ -578,6 +614,30 @@ int launch_decode(kvattn_handle* h, const kvattn::DecodeParams& p, int grid, int
                                          grid, h->stream);
     if (e != hipSuccess)
         return fail(KVATTN_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+    return KVATTN_OK;
+}
+
+// One launch, or one per batch range when the flat range the arguments allow (batch x
+// segments per sequence x the longest attended set, whatever seq_lens holds) exceeds
+// the per-launch limit: the kernels index it in 32 bits.  The ranges are enqueued in
+// order on the handle's stream and share its workspace (each leaves the arrival
+// counters and the unit queue at zero); the grid sized for the whole batch serves each.
+int launch_decode(kvattn_handle* h, const kvattn::DecodeParams& p, int grid, int32_t q_len) {
+    if (grid == 0) return KVATTN_OK;
+    const int64_t per_seq =
+        (int64_t)p.segs_per_seq *
+        std::max<int64_t>(1, max_attended(h->cfg, q_len, p.mask_mode, p.n_sink, p.window));
+    if ((int64_t)p.batch * per_seq <= h->flat_max) return launch_range(h, p, grid, q_len);
+    const int64_t per_launch = h->flat_max / per_seq;
+    if (per_launch < 1)
+        return fail(KVATTN_ERR_CAPACITY,
+                    "one sequence's work (segments x attended positions) exceeds 2^30");
+    for (int64_t b0 = 0; b0 < p.batch; b0 += per_launch) {
+        kvattn::DecodeParams pr = p;
+        batch_range(h, pr, (int32_t)b0, (int32_t)std::min<int64_t>(per_launch, p.batch - b0));
+        const int rc = launch_range(h, pr, grid, q_len);
+        if (rc) return rc;
+    }
     return KVATTN_OK;
 }
 

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v);
     const float c = p.scale_log2;
 
-    for_each_unit(p, fp, wg, n_wg, [&](int64_t ui) __attribute__((always_inline)) {
+    for_each_unit(p, fp, wg, n_wg, [&](int32_t ui) __attribute__((always_inline)) {
     if (p.k_new) append_unit_rows<CACHE, D, 2, PF_THREADS>(p, fp, ui);
     for_each_piece(p, fp, ui, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
     const int b = pc.b;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
         const int nb = wave * PF_RW * 16 + qt * 16 + lr;  // row within the segment
         const bool live = row0 + nb < p.rows;
         const int64_t rid = live ? row_id_of(p, b, kvh, row0 + nb) : 0;
-        const int64_t part = (pc.slot0 + pc.part) * PF_ROWS + nb;
+        const int64_t part = (int64_t)(pc.slot0 + pc.part) * PF_ROWS + nb;
         if (live && pc.nparts > 1 && lq == 0) store_partial_ml(p, part, m[qt], lt);
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {

@@ -26,6 +26,13 @@
 // (a scan over the batch) before its first K/V load, and keeps them in LDS (batches
 // of up to kLenCache sequences), so finding a unit's pieces costs no further memory
 // round trip before the loads.
+//
+// Flat indices are 32-bit: the host launches over batch ranges whose flat range is
+// at most kFlatMax (batch x segments x the longest attended set, whatever seq_lens
+// holds), so every index, unit boundary and slot below fits with room to spare.  The
+// arithmetic runs before a workgroup's first load, one wave per SIMD: 64-bit
+// products, comparisons and divisions cost several instructions each there, and
+// their registers pushed other values out to spill slots.
 #pragma once
 
 #include "device_common.hpp"
@@ -38,30 +45,27 @@ constexpr int kLenCache = 1024;  // sequences whose lengths the plan keeps in LD
 // sequences [b0, b0 + per) and their flat offsets [excl, excl + mine).
 struct FlatPlan {
     const int32_t* lens;  // LDS copy of seq_lens (batch <= kLenCache), else NULL
-    int64_t total;   // W
-    int64_t big;     // positions per head unit
-    int64_t n_big;   // head units: [u * big, (u + 1) * big) for u < n_big
-    int64_t xb;      // n_big * big: where the tail starts (>= total: no tail)
-    int64_t small;   // positions per tail unit
-    int64_t n_units;
+    int32_t total;   // W
+    int32_t big;     // positions per head unit
+    int32_t n_big;   // head units: [u * big, (u + 1) * big) for u < n_big
+    int32_t xb;      // n_big * big: where the tail starts (>= total: no tail)
+    int32_t small;   // positions per tail unit
+    int32_t n_units;
     int b0, per;
-    int64_t excl, mine;
+    int32_t excl, mine;
 };
 
-// Quotient of non-negative 64-bit integers, by a 32-bit division when both fit (the
-// usual case: the full 64-bit division is a long instruction sequence, and the plan
-// and piece arithmetic runs before a workgroup's first load).
-__device__ __forceinline__ int64_t div_nn(int64_t a, int64_t b) {
-    if ((((uint64_t)a | (uint64_t)b) >> 32) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
-    return a / b;
+// Quotient of non-negative integers (an unsigned 32-bit division).
+__device__ __forceinline__ int32_t div_nn(int32_t a, int32_t b) {
+    return (int32_t)((uint32_t)a / (uint32_t)b);
 }
 
 // First flat index of unit u, and the unit holding flat index x (< total): the
 // units partition the range in order, so both are monotone.
-__device__ __forceinline__ int64_t unit_begin(const FlatPlan& f, int64_t u) {
+__device__ __forceinline__ int32_t unit_begin(const FlatPlan& f, int32_t u) {
     return u < f.n_big ? u * f.big : f.xb + (u - f.n_big) * f.small;
 }
-__device__ __forceinline__ int64_t unit_of(const FlatPlan& f, int64_t x) {
+__device__ __forceinline__ int32_t unit_of(const FlatPlan& f, int32_t x) {
     return x < f.xb ? div_nn(x, f.big) : f.n_big + div_nn(x - f.xb, f.small);
 }
 
@@ -71,73 +75,74 @@ __device__ __forceinline__ SeqSpan plan_span(const DecodeParams& p, const FlatPl
 }
 
 // Flat work of sequence b: attended positions x segments per sequence.
-__device__ __forceinline__ int64_t seq_work(const DecodeParams& p, const FlatPlan& f, int b) {
-    return (int64_t)plan_span(p, f, b).count * p.segs_per_seq;
+__device__ __forceinline__ int32_t seq_work(const DecodeParams& p, const FlatPlan& f, int b) {
+    return plan_span(p, f, b).count * p.segs_per_seq;
 }
 
 template <int THREADS>
 __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     static_assert(THREADS % 64 == 0 && THREADS <= 1024, "whole waves");
     constexpr int NW = THREADS / 64;
-    __shared__ int64_t s_part[NW];
+    __shared__ int32_t s_part[NW];
     __shared__ int32_t s_lens[kLenCache];
     const int tid = threadIdx.x;
     FlatPlan f;
     f.lens = nullptr;  // read from seq_lens while the plan is made
     f.per = (p.batch + THREADS - 1) / THREADS;  // sequences per thread
     f.b0 = tid * f.per;
-    int64_t mine = 0;
+    int32_t mine = 0;
     for (int k = 0; k < f.per; ++k) {
         const int b = f.b0 + k;
         if (b < p.batch) {
             const int32_t T = p.seq_lens[b];
             if (p.batch <= kLenCache) s_lens[b] = T;
-            mine += (int64_t)seq_span_of(p, T).count * p.segs_per_seq;
+            mine += seq_span_of(p, T).count * p.segs_per_seq;
         }
     }
     // inclusive scan over the wave, then across waves
     const int lane = tid & 63;
-    int64_t inc = mine;
+    int32_t inc = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const long long y = __shfl_up((long long)inc, o, 64);
+        const int32_t y = __shfl_up(inc, o, 64);
         if (lane >= o) inc += y;
     }
     if (lane == 63) s_part[tid >> 6] = inc;
     __syncthreads();  // s_part and s_lens are complete
     f.lens = p.batch <= kLenCache ? s_lens : nullptr;
-    int64_t before = 0, total = 0;
+    int32_t before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        const int64_t v = s_part[w];
+        const int32_t v = s_part[w];
         before += w < (tid >> 6) ? v : 0;
         total += v;
     }
     f.excl = before + inc - mine;
     f.mine = mine;
     f.total = total;
-    const int64_t units = (int64_t)n_wg * p.units_per_wg;
-    int64_t usz = div_nn(total + units - 1, units);
+    // units_per_wg = 0: units of exactly min_chunk positions (forced unit lengths)
+    const int32_t units = n_wg * p.units_per_wg;
+    int32_t usz = units > 0 ? div_nn(total + units - 1, units) : 0;
     if (usz < p.min_chunk) usz = p.min_chunk;
-    usz = (usz + 15) & ~(int64_t)15;
+    usz = (usz + 15) & ~15;
     // uniform units of usz positions, unless the tail applies: every workgroup has
     // a head unit, and those (>= min_chunk) leave a tail to share
     f.big = usz;
     f.n_big = div_nn(total + usz - 1, usz);
     f.xb = f.n_big * usz;
     f.small = usz;
-    if (p.tail_pct > 0 && f.n_big >= units) {
-        int64_t big = (usz * (100 - p.tail_pct) / 100) & ~(int64_t)15;
-        if (big < p.min_chunk) big = (p.min_chunk + 15) & ~(int64_t)15;
-        if (units * big < total) {
-            const int64_t rest = total - units * big;
-            const int64_t tu = (int64_t)n_wg * p.tail_units;
-            int64_t small = div_nn(rest + tu - 1, tu);
+    if (p.tail_pct > 0 && units > 0 && f.n_big >= units) {
+        int32_t big = (int32_t)(((int64_t)usz * (100 - p.tail_pct) / 100) & ~(int64_t)15);
+        if (big < p.min_chunk) big = (p.min_chunk + 15) & ~15;
+        if ((int64_t)units * big < total) {
+            const int32_t rest = total - units * big;
+            const int32_t tu = n_wg * p.tail_units;
+            int32_t small = div_nn(rest + tu - 1, tu);
             if (small < p.min_chunk) small = p.min_chunk;
             f.big = big;
             f.n_big = units;
             f.xb = units * big;
-            f.small = (small + 15) & ~(int64_t)15;
+            f.small = (small + 15) & ~15;
         }
     }
     f.n_units = f.xb >= total ? div_nn(total + f.big - 1, f.big)
@@ -150,16 +155,16 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
 // exactly one thread matches).  Every thread of the workgroup must call it.
 struct SeqAt {
     int b;
-    int64_t off;
+    int32_t off;
 };
-__device__ __forceinline__ SeqAt seq_at(const DecodeParams& p, const FlatPlan& f, int64_t x) {
+__device__ __forceinline__ SeqAt seq_at(const DecodeParams& p, const FlatPlan& f, int32_t x) {
     __shared__ int32_t s_b;
-    __shared__ int64_t s_off;
+    __shared__ int32_t s_off;
     __syncthreads();  // earlier readers of s_b / s_off are done
     if (f.excl <= x && x < f.excl + f.mine) {
-        int64_t off = f.excl;
+        int32_t off = f.excl;
         for (int k = 0; k < f.per; ++k) {
-            const int64_t w = seq_work(p, f, f.b0 + k);
+            const int32_t w = seq_work(p, f, f.b0 + k);
             if (x < off + w) {
                 s_b = f.b0 + k;
                 s_off = off;
@@ -178,8 +183,8 @@ struct Piece {
     int b;
     int seg;
     int32_t ja, jb;
-    int64_t unit;   // segment id: b * segs_per_seq + seg (its arrival counter)
-    int64_t slot0;  // workspace slot of the segment's first piece
+    int32_t unit;   // segment id: b * segs_per_seq + seg (its arrival counter)
+    int32_t slot0;  // workspace slot of the segment's first piece
     int nparts;     // pieces the segment is cut into (1: this piece writes the output)
     int part;       // this piece's index among them
 };
@@ -191,45 +196,45 @@ struct Piece {
 // current piece's own first loads are in flight.
 template <typename F>
 __device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, const FlatPlan& fp,
-                                                     int64_t u, F&& f) {
-    const int64_t x0 = unit_begin(fp, u);
-    const int64_t x1 = min(unit_begin(fp, u + 1), fp.total);
+                                                     int32_t u, F&& f) {
+    const int32_t x0 = unit_begin(fp, u);
+    const int32_t x1 = min(unit_begin(fp, u + 1), fp.total);
     const SeqAt at = seq_at(p, fp, x0);
     int b = at.b;
-    int64_t off_b = at.off;
+    int32_t off_b = at.off;
     SeqSpan sb = plan_span(p, fp, b);
     // the piece that starts at flat index x (< x1)
-    auto piece_at = [&](int64_t x, Piece& pc, SeqSpan& ps) __attribute__((always_inline)) {
+    auto piece_at = [&](int32_t x, Piece& pc, SeqSpan& ps) __attribute__((always_inline)) {
         // sequences that hold nothing, or that x is already past, are skipped
-        while (x >= off_b + (int64_t)sb.count * p.segs_per_seq) {
-            off_b += (int64_t)sb.count * p.segs_per_seq;
+        while (x >= off_b + sb.count * p.segs_per_seq) {
+            off_b += sb.count * p.segs_per_seq;
             ++b;
             sb = plan_span(p, fp, b);
         }
         pc.b = b;
         pc.seg = (int)div_nn(x - off_b, sb.count);
-        const int64_t seg0 = off_b + (int64_t)pc.seg * sb.count;
-        pc.ja = (int32_t)(x - seg0);
-        pc.jb = (int32_t)min<int64_t>(sb.count, x1 - seg0);
-        const int64_t first = unit_of(fp, seg0);
-        const int64_t last = unit_of(fp, seg0 + sb.count - 1);
-        pc.unit = (int64_t)b * p.segs_per_seq + pc.seg;
+        const int32_t seg0 = off_b + pc.seg * sb.count;
+        pc.ja = x - seg0;
+        pc.jb = min(sb.count, x1 - seg0);
+        const int32_t first = unit_of(fp, seg0);
+        const int32_t last = unit_of(fp, seg0 + sb.count - 1);
+        pc.unit = b * p.segs_per_seq + pc.seg;
         pc.slot0 = first + pc.unit;
-        pc.nparts = (int)(last - first + 1);
-        pc.part = (int)(u - first);
+        pc.nparts = last - first + 1;
+        pc.part = u - first;
         ps = sb;
         return seg0 + pc.jb;  // flat index just past the piece
     };
     if (x0 >= x1) return;
     Piece cur;
     SeqSpan cs;
-    int64_t x = piece_at(x0, cur, cs);
+    int32_t x = piece_at(x0, cur, cs);
     for (;;) {
         const bool more = x < x1;
         bool known = false;
         Piece nx = cur;
         SeqSpan ns = cs;
-        int64_t xn = x;
+        int32_t xn = x;
         auto next = [&](Piece& np, SeqSpan& nps) __attribute__((always_inline)) {
             if (more && !known) xn = piece_at(x, nx, ns);
             known = true;
@@ -249,7 +254,7 @@ __device__ __forceinline__ void for_each_piece_ahead(const DecodeParams& p, cons
 // Calls f(piece, span) for each piece of unit u, in flat order.
 template <typename F>
 __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const FlatPlan& fp,
-                                               int64_t u, F&& f) {
+                                               int32_t u, F&& f) {
     for_each_piece_ahead(p, fp, u,
                          [&](const Piece& pc, const SeqSpan& s, auto&&) __attribute__((always_inline)) {
                              f(pc, s);
@@ -269,15 +274,15 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Flat
 template <typename F>
 __device__ __forceinline__ void for_each_unit(const DecodeParams& p, const FlatPlan& fp, int wg,
                                               int n_wg, F&& body) {
-    __shared__ int64_t s_next_unit[2];  // by iteration parity: a slot is rewritten only
+    __shared__ int32_t s_next_unit[2];  // by iteration parity: a slot is rewritten only
                                         // after a barrier that follows every read of it
     const bool queued = !p.deterministic && fp.n_units > n_wg;
-    int64_t u = wg;
+    int32_t u = wg;
     for (int it = 0; u < fp.n_units; ++it) {
-        int64_t next = 0;
+        int32_t next = 0;
         if (threadIdx.x == 0)  // issued now, its result is waited for only after the unit
             next = !queued ? u + n_wg
-                           : (int64_t)n_wg + __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED,
+                           : n_wg + __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED,
                                                                     __HIP_MEMORY_SCOPE_AGENT);
         body(u);
         if (threadIdx.x == 0) s_next_unit[it & 1] = next;

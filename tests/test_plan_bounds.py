@@ -12,12 +12,12 @@ MIN_CHUNK, MIN_CHUNK_MFMA = 256, 512
 
 
 def plan(total, n_wg, min_chunk, upw=UNITS_PER_WG, tail_pct=TAIL_PCT, tail_units=TAIL_UNITS):
-    units = n_wg * upw
-    usz = max(-(-total // units), min_chunk)
+    units = n_wg * upw  # upw = 0: units of exactly min_chunk (forced unit lengths)
+    usz = max(-(-total // units) if units > 0 else 0, min_chunk)
     usz = (usz + 15) & ~15
     big, n_big, small = usz, -(-total // usz), usz
     xb = n_big * usz
-    if tail_pct > 0 and n_big >= units:
+    if tail_pct > 0 and units > 0 and n_big >= units:
         b = (usz * (100 - tail_pct) // 100) & ~15
         if b < min_chunk:
             b = (min_chunk + 15) & ~15
@@ -102,3 +102,66 @@ def test_tail_takes_the_requested_share():
 def test_small_work_has_no_tail():
     n_units, begin, _ = plan(1000, 256, MIN_CHUNK)
     assert n_units == 4 and begin(1) == 256
+
+
+FLAT_MAX = 1 << 30  # largest flat range of one launch (device_common.hpp: kFlatMax)
+INT32_MAX = (1 << 31) - 1
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_forced_units_are_exactly_min_chunk(seed):
+    # forced unit lengths pass units_per_wg = 0: every unit but the last is min_chunk
+    rng = random.Random(100 + seed)
+    counts = [rng.randint(0, 5000) for _ in range(rng.randint(1, 16))]
+    counts[0] += 1
+    segs = rng.choice([1, 8])
+    mc = rng.choice([64, 256, 1024])
+    total = sum(counts) * segs
+    n_units, begin, unit_of = plan(total, rng.choice([1, 64, 256]), mc, upw=0)
+    assert n_units == -(-total // ((mc + 15) & ~15))
+    assert all(begin(u + 1) - begin(u) == ((mc + 15) & ~15) for u in range(n_units - 1))
+    ps, _ = slots(counts, segs, n_units, begin, unit_of)
+    sl = [p[0] for p in ps]
+    assert len(set(sl)) == len(sl) and max(sl) < n_units + len(counts) * segs
+
+
+@pytest.mark.parametrize("tail", [(0, 2), (15, 2), (25, 4)])
+@pytest.mark.parametrize("n_wg", [1, 2, 255, 256, 1024])
+@pytest.mark.parametrize("mc", [256, 512, 1 << 24])
+def test_plan_indices_fit_32_bits_up_to_the_flat_limit(tail, n_wg, mc):
+    # every value the 32-bit plan forms (work_plan.hpp) stays below 2^31 for flat
+    # ranges up to the per-launch limit: the sums it divides, unit boundaries up to
+    # one past the last unit, and the tail's shares
+    tail_pct, tail_units = tail
+    for total in (1, 15, 16, FLAT_MAX // 3, FLAT_MAX - 1, FLAT_MAX):
+        for upw in (UNITS_PER_WG, 0):
+            units = n_wg * upw
+            usz = max(-(-total // units) if units > 0 else 0, mc)
+            assert total + units - 1 <= INT32_MAX
+            usz = (usz + 15) & ~15
+            assert total + usz - 1 <= INT32_MAX
+            n_units, begin, unit_of = plan(total, n_wg, mc, upw=upw, tail_pct=tail_pct,
+                                           tail_units=tail_units)
+            assert max(begin(n_units), begin(n_units - 1) + usz) <= INT32_MAX
+            # the last unit ends at or past the total, and unit_of inverts begin
+            assert begin(n_units) >= total and unit_of(total - 1) == n_units - 1
+
+
+def batch_ranges(batch, per_seq, flat_max=FLAT_MAX):
+    """kvattn.cpp launch_decode: one launch, or one per batch range of at most
+    flat_max // per_seq sequences (per_seq = segments x the longest attended set)."""
+    if batch * per_seq <= flat_max:
+        return [(0, batch)]
+    per_launch = flat_max // per_seq
+    assert per_launch >= 1
+    return [(b0, min(per_launch, batch - b0)) for b0 in range(0, batch, per_launch)]
+
+
+@pytest.mark.parametrize("batch,per_seq,flat_max", [
+    (1, 1, FLAT_MAX), (4096, 8 * 131072, FLAT_MAX), (256, 16 * 1048576, FLAT_MAX),
+    (7, 1000, 3000), (8, 65536, 131072), (3, 5, 5)])
+def test_batch_ranges_cover_the_batch_within_the_limit(batch, per_seq, flat_max):
+    rs = batch_ranges(batch, per_seq, flat_max)
+    assert [b0 for b0, _ in rs] == list(range(0, batch, rs[0][1]))
+    assert sum(n for _, n in rs) == batch
+    assert all(n >= 1 and n * per_seq <= flat_max for _, n in rs)
