@@ -454,13 +454,13 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             A.w *= vsc;
         }
         const int64_t rid = row_id_of(p, b, kvh, row0 + n);
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         if (pc.nparts == 1) {
-            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
             const uint2 w = {pack2<DT>(A.x * inv, A.y * inv), pack2<DT>(A.z * inv, A.w * inv)};
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
-        } else {
+        } else {  // normalised partial rows
             const int64_t part = (int64_t)(pc.slot0 + pc.part) * NQ + n;
-            store_partial4(p, part * D + d, A);
+            store_partial4<DT>(p, part * D + d, float4{A.x * inv, A.y * inv, A.z * inv, A.w * inv});
             if (d == 0) store_partial_ml(p, part, M, L);
         }
     }

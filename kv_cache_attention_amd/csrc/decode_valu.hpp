@@ -618,7 +618,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
                 store_elem<DT>(p.out, rid * D + d, L > 0.0f ? A / L : 0.0f);
             } else {
                 const int64_t part = (int64_t)(pc.slot0 + pc.part) * ROWS + r;
-                store_partial(p.ws_acc + part * D + d, A);
+                store_partial1<DT>(p, part * D + d, L > 0.0f ? A / L : 0.0f);  // normalised
                 if (d == 0) {
                     store_partial(p.ws_ml + part * 2, M);
                     store_partial(p.ws_ml + part * 2 + 1, L);

@@ -26,7 +26,8 @@ struct DecodeParams {
     const int32_t* block_table;
     const int32_t* seq_lens;
     void* out;
-    float* ws_acc;        // [slots, seg_rows, D]  partials of split segments (unnormalised)
+    float* ws_acc;        // [slots, seg_rows, D]  partial rows of split segments, normalised:
+                          // the query type for 16-bit queries, fp32 for fp32 queries
     float* ws_ml;         // [slots, seg_rows, 2]  (running max m, sum l), log2 domain
     int32_t* counters;    // [batch, Hkv, row blocks] arrivals per segment, 0 between calls
     int32_t* queue;       // [2]: units taken beyond the first per workgroup, workgroups done

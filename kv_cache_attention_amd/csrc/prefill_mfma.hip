@@ -336,17 +336,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
         const int64_t rid = live ? row_id_of(p, b, kvh, row0 + nb) : 0;
         const int64_t part = (int64_t)(pc.slot0 + pc.part) * PF_ROWS + nb;
         if (live && pc.nparts > 1 && lq == 0) store_partial_ml(p, part, m[qt], lt);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {
             if (!live) continue;
             const int d = dt * 16 + lq * 4;
             const f32x4 v = o[dt][qt];
             if (pc.nparts == 1) {
-                const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
                 const uint2 w = {pack2<DT>(v[0] * inv, v[1] * inv), pack2<DT>(v[2] * inv, v[3] * inv)};
                 *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
-            } else {
-                store_partial4(p, part * D + d, float4{v[0], v[1], v[2], v[3]});
+            } else {  // normalised partial rows
+                store_partial4<DT>(p, part * D + d,
+                                   float4{v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv});
             }
         }
     }

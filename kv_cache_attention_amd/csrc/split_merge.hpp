@@ -1,13 +1,17 @@
 // Log-sum-exp merge of split-KV partials, run by the last workgroup of a
 // segment (sequence, KV head, row block) to finish its piece.
 //
-// Each piece k of a segment leaves, per row r, its unnormalised accumulator
-// acc_k[d] and its running max m_k and sum l_k (exp2 domain) in workspace slot
-// slot0 + k, row r (slot-major: index (slot * seg_rows + r)).  The row's result is
-//     M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k acc_k 2^(m_k - M) / L
+// Each piece k of a segment leaves, per row r, its normalised rows o_k[d] = acc_k[d] /
+// l_k and its running max m_k and sum l_k (exp2 domain) in workspace slot slot0 + k,
+// row r (slot-major: index (slot * seg_rows + r)).  The row's result is
+//     M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k l_k 2^(m_k - M) o_k / L
 // - the same rescaling identity the online softmax applies across tiles (Flash
 // Attention section of the nextadmin.net lesson "KV cache and Flash Attention"),
 // applied once more across pieces.  Empty pieces (m = -inf, l = 0) weigh 0.
+//
+// The rows o_k are kept in the query's type for 16-bit queries (rounded to nearest
+// even, half the bytes of fp32: a bounded value, |o_k| <= max |v|, rounded once more
+// than the output is) and in fp32 for fp32 queries; (m_k, l_k) are fp32.
 //
 // Arrival protocol: every workgroup of a segment writes its partial with
 // device-scope stores (they write through the per-XCD L2 to the device-coherent
@@ -53,15 +57,46 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
 constexpr int kCachePolicyDevice = 16;  // SC1
 constexpr int kBufferDword3 = 0x00020000;
 
-// Vector device-scope partial stores (same buffer resources as the reader).
-__device__ __forceinline__ void store_partial4(const DecodeParams& p, int64_t float_index,
-                                               float4 v) {
+// Bits of x in the partial rows' type (16-bit queries).
+template <int DT>
+__device__ __forceinline__ uint32_t part_bits(float x) {
+    return DT == F16 ? f32_to_f16_bits(x) : f32_to_bf16_bits(x);
+}
+template <int DT>
+__device__ __forceinline__ float part_value(uint32_t w16) {
+    if constexpr (DT == F16) return f16_lo(w16);
+    else return bf16_lo(w16);
+}
+
+// Vector device-scope stores of four normalised partial elements starting at element
+// `elem` (same buffer resources as the reader).
+template <int DT>
+__device__ __forceinline__ void store_partial4(const DecodeParams& p, int64_t elem, float4 o) {
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(p.ws_acc, 0, 0x7fffffff, 0x00020000);
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    const u4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
-                  __float_as_uint(v.w)};
-    __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(float_index * 4), 0, 16);
+        __builtin_amdgcn_make_buffer_rsrc(p.ws_acc, 0, 0x7fffffff, kBufferDword3);
+    if constexpr (DT == F32) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        const u4 w = {__float_as_uint(o.x), __float_as_uint(o.y), __float_as_uint(o.z),
+                      __float_as_uint(o.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(elem * 4), 0, kCachePolicyDevice);
+    } else {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const u2 w = {part_bits<DT>(o.x) | (part_bits<DT>(o.y) << 16),
+                      part_bits<DT>(o.z) | (part_bits<DT>(o.w) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)(elem * 2), 0, kCachePolicyDevice);
+    }
+}
+// One normalised partial element.
+template <int DT>
+__device__ __forceinline__ void store_partial1(const DecodeParams& p, int64_t elem, float o) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(p.ws_acc, 0, 0x7fffffff, kBufferDword3);
+    if constexpr (DT == F32)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), r, (int)(elem * 4), 0,
+                                              kCachePolicyDevice);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)part_bits<DT>(o), r, (int)(elem * 2), 0,
+                                              kCachePolicyDevice);
 }
 __device__ __forceinline__ void store_partial_ml(const DecodeParams& p, int64_t part, float m,
                                                  float l) {
@@ -69,7 +104,7 @@ __device__ __forceinline__ void store_partial_ml(const DecodeParams& p, int64_t 
         __builtin_amdgcn_make_buffer_rsrc(p.ws_ml, 0, 0x7fffffff, 0x00020000);
     typedef uint32_t u2 __attribute__((ext_vector_type(2)));
     const u2 w = {__float_as_uint(m), __float_as_uint(l)};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)(part * 8), 0, 16);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)(part * 8), 0, kCachePolicyDevice);
 }
 
 struct PartialReader {
@@ -77,11 +112,20 @@ struct PartialReader {
     __device__ PartialReader(const DecodeParams& p)
         : acc(__builtin_amdgcn_make_buffer_rsrc(p.ws_acc, 0, 0x7fffffff, kBufferDword3)),
           ml(__builtin_amdgcn_make_buffer_rsrc(p.ws_ml, 0, 0x7fffffff, kBufferDword3)) {}
-    __device__ float4 acc4(int64_t float_index) const {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(acc, (int)(float_index * 4), 0,
-                                                             kCachePolicyDevice);
-        return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                      __uint_as_float(v[3])};
+    // four normalised partial elements starting at element `elem`
+    template <int DT>
+    __device__ float4 acc4(int64_t elem) const {
+        if constexpr (DT == F32) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(acc, (int)(elem * 4), 0,
+                                                                 kCachePolicyDevice);
+            return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                          __uint_as_float(v[3])};
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(acc, (int)(elem * 2), 0,
+                                                                kCachePolicyDevice);
+            return float4{part_value<DT>(v[0] & 0xffffu), part_value<DT>(v[0] >> 16),
+                          part_value<DT>(v[1] & 0xffffu), part_value<DT>(v[1] >> 16)};
+        }
     }
     // (m, l) of partial `part`
     __device__ float2 ml2(int64_t part) const {
@@ -167,7 +211,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
 #pragma unroll
             for (int k = 0; k < EPT; ++k) {
                 const int64_t part = part0[k] + (int64_t)spc * NR;
-                v[u][k] = rd.acc4(part * D + (e4[k] % (D / 4)) * 4);
+                v[u][k] = rd.template acc4<DT>(part * D + (e4[k] % (D / 4)) * 4);
                 w[u][k] = rd.ml2(part);
             }
         }
@@ -175,8 +219,11 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
         for (int u = 0; u < US; ++u) {
             const bool in = sp0 + u * SG < nvalid;
 #pragma unroll
-            for (int k = 0; k < EPT; ++k)
-                fold(k, in ? w[u][k].x : NEG_INF, in ? w[u][k].y : 0.0f, v[u][k]);
+            for (int k = 0; k < EPT; ++k) {
+                const float l = in ? w[u][k].y : 0.0f;  // acc = l * o
+                const float4 o = v[u][k];
+                fold(k, in ? w[u][k].x : NEG_INF, l, float4{o.x * l, o.y * l, o.z * l, o.w * l});
+            }
         }
     }
 #pragma unroll
