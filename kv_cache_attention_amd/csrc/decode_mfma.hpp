@@ -425,29 +425,50 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             }
     }
     __syncthreads();
-    // rows out, four d at a time: the final rows (one piece) or this piece's partial
-    for (int idx = tid; idx < NQ * D / 4; idx += MFMA_THREADS) {
+    // rows out, four d at a time: the final rows (one piece) or this piece's partial.
+    // Every chunk's LDS words are read first, then combined: one LDS latency instead of
+    // one per chunk (the accumulators are in LDS now, their registers free).
+    constexpr int CH = NQ * D / 4 / MFMA_THREADS;  // chunks per thread
+    static_assert(CH * MFMA_THREADS == NQ * D / 4, "whole chunks per thread");
+    float cm[CH][MFMA_WAVES], cl[CH][MFMA_WAVES];
+    float4 ca[CH][MFMA_WAVES];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int idx = tid + k * MFMA_THREADS;
+        const int n = idx / (D / 4);
+        const int d = (idx - n * (D / 4)) * 4;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) {
+            cm[k][w] = sm_m[w][n];
+            cl[k][w] = sm_l[w][n];
+            ca[k][w] = *reinterpret_cast<const float4*>(osum + (w * NQ + n) * OROW + d);
+        }
+    }
+    // 8-bit caches: P.V was taken on raw codes, the V scale multiplies the rows
+    const float vsc = KT == FP8 ? p.v_scale[kvh] : 1.0f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int idx = tid + k * MFMA_THREADS;
         const int n = idx / (D / 4);
         const int d = (idx - n * (D / 4)) * 4;
         if (row0 + n >= p.rows) continue;
         float M = NEG_INF;
 #pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, sm_m[w][n]);
+        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, cm[k][w]);
         const float Mu = M == NEG_INF ? 0.0f : M;
         float L = 0.0f;
         float4 A = float4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < MFMA_WAVES; ++w) {
-            const float f = fast_exp2(sm_m[w][n] - Mu);  // 0 for a wave that saw nothing
-            L += sm_l[w][n] * f;
-            const float4 a = *reinterpret_cast<const float4*>(osum + (w * NQ + n) * OROW + d);
+            const float f = fast_exp2(cm[k][w] - Mu);  // 0 for a wave that saw nothing
+            L += cl[k][w] * f;
+            const float4 a = ca[k][w];
             A.x += f * a.x;
             A.y += f * a.y;
             A.z += f * a.z;
             A.w += f * a.w;
         }
-        if constexpr (KT == FP8) {  // 8-bit caches: P.V was taken on raw codes
-            const float vsc = p.v_scale[kvh];
+        if constexpr (KT == FP8) {
             A.x *= vsc;
             A.y *= vsc;
             A.z *= vsc;
