@@ -133,7 +133,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             const int32_t j = min(tb + tt * 16 + lr, j1 - 1);
             Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
             L.unit = L.unit >= 0 ? L.unit : 0;
-            const int64_t off = row_offset(p, L, kvh) + lq * 8;
+            const int64_t off = row_offset<CACHE>(p, L, kvh) + lq * 8;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kf[tt][ks] = kv_words<KT, DT>(kp + (off + ks * 32) * EB);
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
             Loc L = locate<CACHE>(p, s, b, span_pos(s, j));
             vok[v] = L.unit >= 0;
             L.unit = L.unit >= 0 ? L.unit : 0;
-            vf[v] = kv_words<KT, DT>(vp + (row_offset(p, L, kvh) + (l % CPR) * 8) * EB);
+            vf[v] = kv_words<KT, DT>(vp + (row_offset<CACHE>(p, L, kvh) + (l % CPR) * 8) * EB);
         }
     };
 

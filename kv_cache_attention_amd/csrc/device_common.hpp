@@ -161,9 +161,18 @@ __device__ __forceinline__ Loc paged_loc(const DecodeParams& p, int32_t blk, int
     return l;
 }
 
-// Element offset of the (location, KV head) row of a cache.
+// Element offset of the (location, KV head) row of a cache.  Slot indices are
+// non-negative and the strides of a position and of a page block are below 2^32 (the
+// host checks the block's at create), so a lane's share is one 32 x 32 -> 64-bit
+// product; the sequence's and the head's shares are the same across the workgroup.
+template <int CACHE>
 __device__ __forceinline__ int64_t row_offset(const DecodeParams& p, const Loc& l, int kvh) {
-    return l.unit * p.stride_seq + (int64_t)kvh * p.stride_head + (int64_t)l.idx * p.stride_tok;
+    const uint64_t slot = (uint64_t)(uint32_t)l.idx * (uint32_t)p.stride_tok;
+    if constexpr (CACHE == PAGED)
+        return (int64_t)((uint64_t)(uint32_t)l.unit * (uint32_t)p.stride_seq + slot) +
+               (int64_t)kvh * p.stride_head;
+    else
+        return l.unit * p.stride_seq + (int64_t)kvh * p.stride_head + (int64_t)slot;
 }
 
 // Flat slot index, independent of the layout: b * capacity + slot, or

@@ -48,7 +48,7 @@ __device__ __forceinline__ void append_unit_rows(const DecodeParams& p, const Fl
             if (L.unit < 0) continue;
             const int64_t src =
                 (((int64_t)pc.b * p.q_len + (pos - tn)) * p.num_kv_heads + kvh) * RB + ch * 16;
-            const int64_t dst = row_offset(p, L, kvh) * EB + ch * 16;
+            const int64_t dst = row_offset<CACHE>(p, L, kvh) * EB + ch * 16;
             const uint4 kx = *reinterpret_cast<const uint4*>(p.k_new + src);
             const uint4 vx = *reinterpret_cast<const uint4*>(p.v_new + src);
             *reinterpret_cast<uint4*>(kc + dst) = kx;

@@ -158,6 +158,9 @@ int validate_config(const kvattn_config* c) {
     if (c->num_q_heads < 1 || c->num_kv_heads < 1 || c->num_q_heads % c->num_kv_heads)
         return fail(KVATTN_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
     if (c->max_batch < 1) return fail(KVATTN_ERR_INVALID_ARG, "max_batch must be >= 1");
+    // the kernels address a position's row in 32 bits (bytes)
+    if ((int64_t)c->num_kv_heads * c->head_dim * 4 >= (int64_t)1 << 32)
+        return fail(KVATTN_ERR_UNSUPPORTED, "num_kv_heads too large");
     if (c->max_q_len < 1 || c->max_q_len > kMaxQLen)
         return fail(KVATTN_ERR_UNSUPPORTED, "max_q_len must be in 1..1024");
     if (c->capacity < 1) return fail(KVATTN_ERR_INVALID_ARG, "capacity must be >= 1");
@@ -181,6 +184,9 @@ int validate_config(const kvattn_config* c) {
         if (c->capacity % c->block_size)
             return fail(KVATTN_ERR_INVALID_ARG, "capacity must be a multiple of block_size");
         if (c->num_blocks < 1) return fail(KVATTN_ERR_INVALID_ARG, "num_blocks must be >= 1");
+        // the kernels address within a block in 32 bits (bytes)
+        if ((int64_t)c->block_size * c->num_kv_heads * c->head_dim * 4 >= (int64_t)1 << 32)
+            return fail(KVATTN_ERR_UNSUPPORTED, "block_size x num_kv_heads x head_dim too large");
         break;
     default:
         return fail(KVATTN_ERR_INVALID_ARG, "unknown cache_mode");

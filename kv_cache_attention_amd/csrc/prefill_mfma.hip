@@ -141,7 +141,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_mfma_kernel(const Decod
                 stage.ok |= (L.unit >= 0 ? 1u : 0u) << k;
                 L.unit = L.unit >= 0 ? L.unit : 0;
             }
-            const int64_t off = row_offset(p, L, kvh) + (rem % CPR) * 8;
+            const int64_t off = row_offset<CACHE>(p, L, kvh) + (rem % CPR) * 8;
             stage.w[k] = *reinterpret_cast<const u32x4*>((kind ? vp : kp) + off);
         }
     };
