@@ -205,7 +205,9 @@ KVATTN_API int kvattn_append(kvattn_handle* h, const void* k_new, const void* v_
  * (the new positions are the last of every attended list, and no attended position
  * shares a slot with a new one), so no step-wide ordering is needed.  Arguments as
  * for the two calls; a RING cache uses n_sink for both (with
- * KVATTN_MASK_SINK_WINDOW).  k_new / v_new must not overlap the caches. */
+ * KVATTN_MASK_SINK_WINDOW).  k_new / v_new must not overlap the caches.  Launches
+ * over batch ranges as kvattn_decode does, each range writing its own sequences'
+ * rows. */
 KVATTN_API int kvattn_append_decode(kvattn_handle* h, const void* q, const void* k_new,
                                     const void* v_new, void* k_cache, void* v_cache,
                                     const int32_t* block_table, const int32_t* seq_lens,

@@ -1,7 +1,8 @@
 // C-ABI host side of kvattn: argument validation, work decomposition, the
 // handle's workspace, and the launches on the caller's stream.  kvattn_create
 // allocates and clears the workspace (and waits for the clear); kvattn_decode
-// allocates nothing and never synchronises: one kernel launch per call.
+// allocates nothing and never synchronises: one kernel launch per call (one per batch
+// range when the call's flat range exceeds 2^30 position units).
 #include "../../include/kvattn.h"
 
 #include <hip/hip_runtime.h>
