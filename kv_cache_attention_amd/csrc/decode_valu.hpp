@@ -478,15 +478,18 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void decode_valu_kernel(const Decod
 #pragma unroll
                 for (int u = 0; u < U; ++u) ka[u] = x.klast;
             } else {
-                // paged: the row lane 0 read (a valid address), one chunk per instruction
-                // (readfirstlane returns a signed int: each half is widened through
-                // uint32_t, so a low half with bit 31 set does not sign-extend)
-                const uint64_t a0 = (uint64_t)ka[0];
-                const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a0 >> 32));
-                const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a0);
-                const uint64_t a = ((uint64_t)hi << 32) | (uint64_t)lo;
+                // paged: the row lane 0 read (a valid address), one chunk per instruction.
+                // Its offset from the cache base is broadcast, not the address itself, so
+                // the loads keep the base's global provenance (an address rebuilt from an
+                // integer would make them flat loads, which the compiler can only wait for
+                // all at once).  readfirstlane returns a signed int: each half is widened
+                // through uint32_t, so a low half with bit 31 set does not sign-extend.
+                const uint64_t o0 = (uint64_t)(ka[0] - x.kb);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(o0 >> 32));
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)o0);
+                const uint64_t o = ((uint64_t)hi << 32) | (uint64_t)lo;
 #pragma unroll
-                for (int u = 0; u < U; ++u) ka[u] = reinterpret_cast<const char*>(a);
+                for (int u = 0; u < U; ++u) ka[u] = x.kb + o;
             }
             int32_t n2 = n_tiles;
             if constexpr (CACHE == PAGED) {
