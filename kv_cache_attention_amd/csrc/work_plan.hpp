@@ -43,8 +43,12 @@ constexpr int kLenCache = 1024;  // sequences whose lengths the plan keeps in LD
 
 // Per-thread view of the flat range after the scan over the batch: thread t owns
 // sequences [b0, b0 + per) and their flat offsets [excl, excl + mine).
+typedef const int32_t __attribute__((address_space(3)))* lds_i32_ptr;
 struct FlatPlan {
-    const int32_t* lens;  // LDS copy of seq_lens (batch <= kLenCache), else NULL
+    // LDS copy of seq_lens (batch <= kLenCache), typed as LDS so reads of it are LDS
+    // reads (a generic pointer would make them flat loads, waited for with every load)
+    lds_i32_ptr lens;
+    bool has_lens;
     int32_t total;   // W
     int32_t big;     // positions per head unit
     int32_t n_big;   // head units: [u * big, (u + 1) * big) for u < n_big
@@ -71,7 +75,7 @@ __device__ __forceinline__ int32_t unit_of(const FlatPlan& f, int32_t x) {
 
 // Span of sequence b, from the plan's LDS copy of the lengths when it has one.
 __device__ __forceinline__ SeqSpan plan_span(const DecodeParams& p, const FlatPlan& f, int b) {
-    return f.lens ? seq_span_of(p, f.lens[b]) : seq_span(p, b);
+    return f.has_lens ? seq_span_of(p, f.lens[b]) : seq_span(p, b);
 }
 
 // Flat work of sequence b: attended positions x segments per sequence.
@@ -87,7 +91,8 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     __shared__ int32_t s_lens[kLenCache];
     const int tid = threadIdx.x;
     FlatPlan f;
-    f.lens = nullptr;  // read from seq_lens while the plan is made
+    f.has_lens = false;  // read from seq_lens while the plan is made
+    f.lens = (lds_i32_ptr)s_lens;
     f.per = (p.batch + THREADS - 1) / THREADS;  // sequences per thread
     f.b0 = tid * f.per;
     int32_t mine = 0;
@@ -109,7 +114,7 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     }
     if (lane == 63) s_part[tid >> 6] = inc;
     __syncthreads();  // s_part and s_lens are complete
-    f.lens = p.batch <= kLenCache ? s_lens : nullptr;
+    f.has_lens = p.batch <= kLenCache;
     int32_t before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
