@@ -91,6 +91,8 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     __shared__ u32x4 qsm[G::QFRAGS * 64];
     __shared__ float sm_m[MFMA_WAVES][NQ];
     __shared__ float sm_l[MFMA_WAVES][NQ];
+    __shared__ float4 sm_wt[NQ];  // row n's weights of the four waves' accumulators
+    __shared__ float2 sm_ml[NQ];  // row n's (max, sum) over the four waves
 
     // the tile counter in word 0; lanes 1 .. 63 of the all-lane atomic hit words 1 .. 63
     // (adding 0), so one atomic never sends 64 lanes to one LDS bank
@@ -400,9 +402,11 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         nxt = n2;
     }
 
-    // ---- merge the four waves: each wave leaves its row sums and its unscaled O in
-    // a slot of LDS (one barrier), then every output element combines the four with
-    // the factors 2^(m_w - M), M = the largest of the four running maxima
+    // ---- merge the four waves: each wave leaves its row maxima and sums in LDS (one
+    // barrier), then its unscaled O; meanwhile one thread per row works out the row's
+    // weights w_w = 2^(m_w - M) / L (M the largest of the four running maxima, L the sum
+    // of the l_w 2^(m_w - M)), so that after the second barrier every output element is
+    // sum_w w_w O_w: four fused multiply-adds a wave, no exponentials
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
         const float lt = xsum_16_32(lsum[qt]);
@@ -424,72 +428,78 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
                     float4{v[0], v[1], v[2], v[3]};
             }
     }
+    static_assert(MFMA_WAVES == 4, "a float4 of weights per row");
+    if (tid < NQ) {
+        float mw[MFMA_WAVES], M = NEG_INF;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) {
+            mw[w] = sm_m[w][tid];
+            M = fmaxf(M, mw[w]);
+        }
+        const float Mu = M == NEG_INF ? 0.0f : M;
+        float e[MFMA_WAVES], L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) {
+            e[w] = fast_exp2(mw[w] - Mu);  // 0 for a wave that saw nothing
+            L += sm_l[w][tid] * e[w];
+        }
+        // 8-bit caches: P.V was taken on raw codes, the V scale multiplies the rows
+        const float inv = L > 0.0f ? (KT == FP8 ? p.v_scale[kvh] : 1.0f) / L : 0.0f;
+        sm_wt[tid] = float4{e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv};
+        sm_ml[tid] = float2{M, L};
+    }
     __syncthreads();
     // rows out, four d at a time: the final rows (one piece) or this piece's partial.
     // Every chunk's LDS words are read first, then combined: one LDS latency instead of
     // one per chunk (the accumulators are in LDS now, their registers free).
     constexpr int CH = NQ * D / 4 / MFMA_THREADS;  // chunks per thread
     static_assert(CH * MFMA_THREADS == NQ * D / 4, "whole chunks per thread");
-    float cm[CH][MFMA_WAVES], cl[CH][MFMA_WAVES];
+    float4 cw[CH];
     float4 ca[CH][MFMA_WAVES];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
         const int idx = tid + k * MFMA_THREADS;
         const int n = idx / (D / 4);
         const int d = (idx - n * (D / 4)) * 4;
+        cw[k] = sm_wt[n];
 #pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) {
-            cm[k][w] = sm_m[w][n];
-            cl[k][w] = sm_l[w][n];
+        for (int w = 0; w < MFMA_WAVES; ++w)
             ca[k][w] = *reinterpret_cast<const float4*>(osum + (w * NQ + n) * OROW + d);
-        }
     }
-    // 8-bit caches: P.V was taken on raw codes, the V scale multiplies the rows
-    const float vsc = KT == FP8 ? p.v_scale[kvh] : 1.0f;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
         const int idx = tid + k * MFMA_THREADS;
         const int n = idx / (D / 4);
         const int d = (idx - n * (D / 4)) * 4;
         if (row0 + n >= p.rows) continue;
-        float M = NEG_INF;
-#pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) M = fmaxf(M, cm[k][w]);
-        const float Mu = M == NEG_INF ? 0.0f : M;
-        float L = 0.0f;
+        const float wv[MFMA_WAVES] = {cw[k].x, cw[k].y, cw[k].z, cw[k].w};
         float4 A = float4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < MFMA_WAVES; ++w) {
-            const float f = fast_exp2(cm[k][w] - Mu);  // 0 for a wave that saw nothing
-            L += cl[k][w] * f;
             const float4 a = ca[k][w];
-            A.x += f * a.x;
-            A.y += f * a.y;
-            A.z += f * a.z;
-            A.w += f * a.w;
+            A.x = fmaf(wv[w], a.x, A.x);
+            A.y = fmaf(wv[w], a.y, A.y);
+            A.z = fmaf(wv[w], a.z, A.z);
+            A.w = fmaf(wv[w], a.w, A.w);
         }
-        if constexpr (KT == FP8) {
-            A.x *= vsc;
-            A.y *= vsc;
-            A.z *= vsc;
-            A.w *= vsc;
-        }
-        const int64_t rid = row_id_of(p, b, kvh, row0 + n);
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         if (pc.nparts == 1) {
-            const uint2 w = {pack2<DT>(A.x * inv, A.y * inv), pack2<DT>(A.z * inv, A.w * inv)};
+            const int64_t rid = row_id_of(p, b, kvh, row0 + n);
+            const uint2 w = {pack2<DT>(A.x, A.y), pack2<DT>(A.z, A.w)};
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + rid * D + d) = w;
         } else {  // normalised partial rows
             const int64_t part = (int64_t)(pc.slot0 + pc.part) * NQ + n;
-            store_partial4<DT>(p, part * D + d, float4{A.x * inv, A.y * inv, A.z * inv, A.w * inv});
-            if (d == 0) store_partial_ml(p, part, M, L);
+            store_partial4<DT>(p, part * D + d, A);
+            if (d == 0) {
+                const float2 ml = sm_ml[n];
+                store_partial_ml(p, part, ml.x, ml.y);
+            }
         }
     }
     // the staging area is free again: the merge's scratch lives there
-    static_assert(sizeof(MergeSmem<NQ, MFMA_THREADS>) <= SMEM, "merge scratch");
+    static_assert(sizeof(MergeSmem<NQ, MFMA_THREADS, true>) <= SMEM, "merge scratch");
     __syncthreads();
     if (pc.nparts > 1) {
-        auto& msm = *reinterpret_cast<MergeSmem<NQ, MFMA_THREADS>*>(smem);
+        auto& msm = *reinterpret_cast<MergeSmem<NQ, MFMA_THREADS, true>*>(smem);
         arrive_and_merge<DT, D, NQ, MFMA_THREADS>(p, b, kvh, row0, pc.unit, pc.slot0, pc.nparts,
                                                   msm);
         __syncthreads();  // LDS is reused by the next piece

@@ -156,17 +156,6 @@ __device__ __forceinline__ void unpack16(const typename KVec<KT>::T& w, float* f
     }
 }
 
-// two fp32 -> one dword of two 16-bit values of type DT (round to nearest even)
-template <int DT>
-__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    const f32x2_t v = {lo, hi};
-    if constexpr (DT == F16)
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
-    else
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
 // acc[r][e] += sum_u p[r][u] * v[u][e] for 8-bit V codes (unscaled), two positions
 // per packed dot product: a byte permute interleaves the codes of positions u and
 // u+1, one exact conversion gives the (v[u][e], v[u+1][e]) pair in the query's

@@ -68,6 +68,20 @@ __device__ __forceinline__ float part_value(uint32_t w16) {
     else return bf16_lo(w16);
 }
 
+// Two floats as a pair of 16-bit values (lo in the low half), rounded to nearest even
+// by the conversion instructions.
+template <int DT>
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    if constexpr (DT == F16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
 // Vector device-scope stores of four normalised partial elements starting at element
 // `elem` (same buffer resources as the reader).
 template <int DT>
@@ -81,8 +95,7 @@ __device__ __forceinline__ void store_partial4(const DecodeParams& p, int64_t el
         __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(elem * 4), 0, kCachePolicyDevice);
     } else {
         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-        const u2 w = {part_bits<DT>(o.x) | (part_bits<DT>(o.y) << 16),
-                      part_bits<DT>(o.z) | (part_bits<DT>(o.w) << 16)};
+        const u2 w = {pack_pair<DT>(o.x, o.y), pack_pair<DT>(o.z, o.w)};
         __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)(elem * 2), 0, kCachePolicyDevice);
     }
 }
@@ -135,17 +148,31 @@ struct PartialReader {
     }
 };
 
-// Shared memory the merge needs (floats).
-template <int NROWS, int THREADS>
+// Partials per segment up to which the merge computes each row's weights once (and
+// keeps them in LDS); beyond it, it folds the partials in with the running rescaling.
+constexpr int kWeightParts = 16;
+
+// Shared memory the merge needs (floats); W: with room for the two-pass form's weights.
+template <int NROWS, int THREADS, bool W = false>
 struct MergeSmem {
-    float4 red[THREADS];     // split groups' accumulators ...
-    float2 red_ml[THREADS];  // ... and their running (max, sum)
+    float4 red[THREADS];                 // split groups' accumulators ...
+    float2 red_ml[THREADS];              // ... and their running (max, sum)
+    float w[W ? NROWS : 1][kWeightParts];  // row r's weight of partial k
 };
 
-// Merges the nvalid partials of rows row0 .. row0 + NROWS - 1 of KV head kvh
-// (rows roff .. of slots slot0 ..) into the output and puts the segment's counter
-// back to zero.  Called by every thread of the workgroup that drew the segment's
-// last ticket.
+// Four consecutive output elements, rounded to nearest even, in one store (the output
+// and every row of it are 16-byte aligned).
+template <int DT>
+__device__ __forceinline__ void store_out4(void* out, int64_t idx, float4 v) {
+    if constexpr (DT == F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = v;
+    } else {
+        const uint2 w = {pack_pair<DT>(v.x, v.y), pack_pair<DT>(v.z, v.w)};
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = w;
+    }
+}
+
+// The merge of more than kWeightParts partials (merge_partials below).
 //
 // One pass over the partials: each thread owns float4 chunks of (row, d) - split
 // groups share the threads left over - and folds the partials in as it reads them,
@@ -154,10 +181,10 @@ struct MergeSmem {
 // Every load of a step (US partials x the thread's chunks, accumulators and (max,
 // sum) words together) is issued before any is used, so a merge of up to US x split
 // groups partials costs one memory latency.
-template <int DT, int D, int NROWS, int THREADS>
-__device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int kvh, int row0,
-                                               int64_t unit, int64_t slot0, int nvalid,
-                                               MergeSmem<NROWS, THREADS>& sm, int roff = 0) {
+template <int DT, int D, int NROWS, int THREADS, bool W>
+__device__ __forceinline__ void merge_online(const DecodeParams& p, int b, int kvh, int row0,
+                                             int64_t slot0, int nvalid,
+                                             MergeSmem<NROWS, THREADS, W>& sm, int roff) {
     static_assert(THREADS % 64 == 0, "whole waves");
     const int tid = threadIdx.x;
     constexpr float NEG_INF = -__builtin_inff();
@@ -248,7 +275,144 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int
             store_elem<DT>(p.out, o + 3, a[k].w * inv);
         }
     }
-    if (tid == 0) atomicExch(p.counters + unit, 0);  // ready for the next call
+}
+
+// The same merge in two passes, for up to kWeightParts partials: one thread per row
+// reads the row's (max, sum) words and computes its weights
+//     w_k = l_k 2^(m_k - M) / L,   M = max_k m_k,  L = sum_k l_k 2^(m_k - M)
+// once, into LDS; then every output element is sum_k w_k o_k - four fused multiply-adds
+// per partial for four elements, where the running rescaling costs two exponentials, a
+// maximum and a dozen multiplies per partial and element group.  The rows of the
+// first partials are requested before the weights are worked out, so their latency and
+// that of the (max, sum) words overlap.
+template <int DT, int D, int NROWS, int THREADS>
+__device__ __forceinline__ void merge_weighted(const DecodeParams& p, int b, int kvh, int row0,
+                                               int64_t slot0, int nvalid,
+                                               MergeSmem<NROWS, THREADS, true>& sm, int roff) {
+    static_assert(THREADS % 64 == 0 && NROWS <= THREADS, "whole waves, a thread per row");
+    const int tid = threadIdx.x;
+    constexpr float NEG_INF = -__builtin_inff();
+    constexpr int KW = kWeightParts;
+    const int NR = p.seg_rows;  // partial k of row r: index (slot0 + k) * NR + r
+    const PartialReader rd(p);
+
+    constexpr int E4 = NROWS * D / 4;
+    constexpr int SG = E4 >= THREADS ? 1 : THREADS / E4;
+    constexpr int EPT = E4 >= THREADS ? (E4 + THREADS - 1) / THREADS : 1;
+    constexpr int US = 4;  // partials per step
+    static_assert(E4 >= THREADS || THREADS % E4 == 0, "shape");
+    static_assert(SG == 1 || EPT == 1, "split groups hold one chunk each");
+    const int sg = E4 >= THREADS ? 0 : tid / E4;
+    int e4[EPT], r[EPT];
+    bool live[EPT];
+    int64_t part0[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = E4 >= THREADS ? tid + k * THREADS : tid % E4;
+        const bool in = e < E4;
+        e4[k] = in ? e : 0;
+        r[k] = e4[k] / (D / 4);
+        live[k] = in && row0 + r[k] < p.rows;
+        part0[k] = live[k] ? slot0 * NR + roff + r[k] : 0;
+    }
+    // partials sg, sg + SG, ... of this thread's chunks, US at a time (past nvalid:
+    // partial 0 again, weighted 0)
+    float4 v[US][EPT];
+    auto load_step = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const int kk = k0 + u * SG;
+            const int kc = kk < nvalid ? kk : 0;
+#pragma unroll
+            for (int k = 0; k < EPT; ++k)
+                v[u][k] = rd.template acc4<DT>((part0[k] + (int64_t)kc * NR) * D +
+                                               (e4[k] % (D / 4)) * 4);
+        }
+    };
+    load_step(sg);
+
+    if (tid < NROWS && row0 + tid < p.rows) {
+        float2 ml[KW];
+#pragma unroll
+        for (int k = 0; k < KW; ++k)
+            ml[k] = k < nvalid ? rd.ml2((slot0 + k) * NR + roff + tid) : float2{NEG_INF, 0.0f};
+        float M = NEG_INF;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) M = fmaxf(M, ml[k].x);
+        const float Mu = M == NEG_INF ? 0.0f : M;
+        float e[KW], L = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            e[k] = ml[k].y * fast_exp2(ml[k].x - Mu);  // 0 for an empty piece or k >= nvalid
+            L += e[k];
+        }
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) sm.w[tid][k] = e[k] * inv;
+    }
+    __syncthreads();  // the weights are in LDS
+
+    float4 a[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) a[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto accumulate = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const int kk = k0 + u * SG;
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const float w = kk < nvalid ? sm.w[r[k]][kk] : 0.0f;
+                a[k].x = fmaf(w, v[u][k].x, a[k].x);
+                a[k].y = fmaf(w, v[u][k].y, a[k].y);
+                a[k].z = fmaf(w, v[u][k].z, a[k].z);
+                a[k].w = fmaf(w, v[u][k].w, a[k].w);
+            }
+        }
+    };
+    accumulate(sg);
+    for (int k0 = sg + US * SG; k0 < nvalid; k0 += US * SG) {
+        load_step(k0);
+        accumulate(k0);
+    }
+    if constexpr (SG > 1) {  // the split groups' sums, in group order
+        sm.red[tid] = a[0];
+        __syncthreads();
+        if (sg == 0) {
+            for (int g2 = 1; g2 < SG; ++g2) {
+                const float4 o = sm.red[g2 * E4 + e4[0]];
+                a[0].x += o.x;
+                a[0].y += o.y;
+                a[0].z += o.z;
+                a[0].w += o.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+        if (sg == 0 && live[k])
+            store_out4<DT>(p.out, row_id_of(p, b, kvh, row0 + r[k]) * D + (e4[k] % (D / 4)) * 4,
+                           a[k]);
+}
+
+// Merges the nvalid partials of rows row0 .. row0 + NROWS - 1 of KV head kvh (rows
+// roff .. of slots slot0 ..) into the output and puts the segment's counter back to
+// zero.  Called by every thread of the workgroup that drew the segment's last ticket.
+// With a scratch that has room for weights (W), the two-pass form where it applies: the
+// matrix-core decode kernel, whose registers hold both forms (in the vector-ALU
+// kernels the second form pushed scalar values out of registers inside the tile loop).
+template <int DT, int D, int NROWS, int THREADS, bool W>
+__device__ __forceinline__ void merge_partials(const DecodeParams& p, int b, int kvh, int row0,
+                                               int64_t unit, int64_t slot0, int nvalid,
+                                               MergeSmem<NROWS, THREADS, W>& sm, int roff = 0) {
+    bool done = false;
+    if constexpr (W) {
+        if (nvalid <= kWeightParts) {
+            merge_weighted<DT, D, NROWS, THREADS>(p, b, kvh, row0, slot0, nvalid, sm, roff);
+            done = true;
+        }
+    }
+    if (!done) merge_online<DT, D, NROWS, THREADS>(p, b, kvh, row0, slot0, nvalid, sm, roff);
+    if (threadIdx.x == 0) atomicExch(p.counters + unit, 0);  // ready for the next call
 }
 
 // Called by every thread of the workgroup after it wrote its partial into slot
@@ -264,9 +428,9 @@ __device__ __forceinline__ bool arrive(const DecodeParams& p, int64_t unit, int 
 }
 
 // arrive, then (last workgroup of the segment) merge rows row0 .. row0 + NROWS - 1.
-template <int DT, int D, int NROWS, int THREADS>
+template <int DT, int D, int NROWS, int THREADS, bool W>
 __device__ __forceinline__ void arrive_and_merge(const DecodeParams& p, int b, int kvh, int row0, int64_t unit,
-                                 int64_t slot0, int nvalid, MergeSmem<NROWS, THREADS>& sm) {
+                                 int64_t slot0, int nvalid, MergeSmem<NROWS, THREADS, W>& sm) {
     if (arrive(p, unit, nvalid))
         merge_partials<DT, D, NROWS, THREADS>(p, b, kvh, row0, unit, slot0, nvalid, sm);
 }
