@@ -260,7 +260,11 @@ __device__ __forceinline__ void merge_online(const DecodeParams& p, int b, int k
             sm.red_ml[tid] = float2{mx[k], ls[k]};
             __syncthreads();
             if (sg == 0) {
-                for (int g2 = 1; g2 < SG; ++g2) {
+                // groups g >= nvalid were given no partial: their state is empty and
+                // folding it in changes nothing (factor 1 on the sum, 0 on it), so with
+                // many groups (one or two rows) the fold stops at nvalid
+                const int ng = SG > 4 ? (nvalid < SG ? nvalid : SG) : SG;
+                for (int g2 = 1; g2 < ng; ++g2) {
                     const float2 o = sm.red_ml[g2 * E4 + e4[k]];
                     fold(k, o.x, o.y, sm.red[g2 * E4 + e4[k]]);
                 }
@@ -378,7 +382,7 @@ __device__ __forceinline__ void merge_weighted(const DecodeParams& p, int b, int
         sm.red[tid] = a[0];
         __syncthreads();
         if (sg == 0) {
-            for (int g2 = 1; g2 < SG; ++g2) {
+            for (int g2 = 1; g2 < SG && g2 < nvalid; ++g2) {  // later groups hold zeros
                 const float4 o = sm.red[g2 * E4 + e4[0]];
                 a[0].x += o.x;
                 a[0].y += o.y;
