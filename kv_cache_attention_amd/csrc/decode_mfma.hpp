@@ -28,7 +28,7 @@
 // The next tile's V is loaded as soon as this tile's V sits in LDS, its K as soon
 // as S^T has consumed this tile's K, so both are in flight during the rest.  The
 // four waves then merge through LDS and the workgroup writes the final rows (its
-// sequence needs one split) or its partial (acc, m, l); the last workgroup of the
+// sequence needs one split) or its partial (normalised rows, m, l); the last workgroup of the
 // (sequence, KV head) merges the partials (split_merge.hpp).
 #pragma once
 

@@ -23,7 +23,7 @@
 // (scale * log2 e folded into one multiply).  At the end of a piece the lane
 // groups of a wave merge through cross-lane shuffles, the waves through LDS, and
 // the workgroup writes either the final rows (the piece is a whole segment) or
-// its unnormalised partial (acc, m, l); the last piece of a segment to finish
+// its partial (normalised rows, running max and sum); the last piece of a segment to finish
 // merges the partials (split_merge.hpp).
 //
 // Loads are rolling: a wave issues the next tile's K as soon as the current

@@ -177,7 +177,7 @@ __device__ __forceinline__ void store_out4(void* out, int64_t idx, float4 v) {
 // One pass over the partials: each thread owns float4 chunks of (row, d) - split
 // groups share the threads left over - and folds the partials in as it reads them,
 // with the same rescaling identity:
-//     M' = max(M, m_k),  L' = L 2^(M - M') + l_k 2^(m_k - M'),  A' = A 2^(M - M') + acc_k 2^(m_k - M').
+//     M' = max(M, m_k),  L' = L 2^(M - M') + l_k 2^(m_k - M'),  A' = A 2^(M - M') + l_k o_k 2^(m_k - M').
 // Every load of a step (US partials x the thread's chunks, accumulators and (max,
 // sum) words together) is issued before any is used, so a merge of up to US x split
 // groups partials costs one memory latency.

@@ -7,15 +7,17 @@
 // W = sum_b count_b * segs_per_seq position-units, cut into units for a grid
 // sized by the host to what the GPU holds at once.  The head of the range is cut
 // into one large unit per workgroup (units_per_wg of them), which each workgroup
-// takes first; the last tail_pct percent into about tail_units smaller units per
-// workgroup, handed out by a device-wide queue to whichever workgroup is free.
-// Compute units are served by the memory system at rates that differ by 10-20 %
-// (from one die to the next, and within a die), so equal static shares end when
-// the slowest finishes; with the tail, the ones served faster take more of it.
+// takes first; optionally (tail_pct > 0, a build setting that is off by default) the
+// last tail_pct percent into about tail_units smaller units per workgroup, handed out
+// by a device-wide queue to whichever workgroup is free.  Compute units are served by
+// the memory system at rates that differ by several percent, so equal static shares
+// end when the slowest finishes; a tail would let the faster ones take more of it,
+// but each extra unit costs a piece epilogue and a ramp, which measured more than
+// the spread it removed.
 //
 // A unit crosses segment boundaries: its pieces are processed one after the
 // other.  A piece that is a whole segment writes the final rows; otherwise it
-// writes a partial (unnormalised accumulator, running max and sum) and the last
+// writes a partial (normalised rows, running max and sum) and the last
 // piece of the segment to finish merges them (split_merge.hpp).  Walking the
 // pieces in flat order, both the unit index and the segment index never decrease
 // and at least one grows at each step, so slot = unit + segment is a distinct
