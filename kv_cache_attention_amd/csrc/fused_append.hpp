@@ -31,7 +31,7 @@ __device__ __forceinline__ void append_unit_rows(const DecodeParams& p, const Fl
     char* kc = const_cast<char*>(reinterpret_cast<const char*>(p.k));
     char* vc = const_cast<char*>(reinterpret_cast<const char*>(p.v));
     for_each_piece(p, fp, u, [&](const Piece& pc, const SeqSpan& s) __attribute__((always_inline)) {
-        int32_t T = fp.has_lens ? fp.lens[pc.b] : p.seq_lens[pc.b];
+        int32_t T = plan_len(p, fp, pc.b);
         if (T < 0) T = 0;
         const int32_t tn = T - p.q_len;  // first new position
         // work index of the first new position (the new positions end the list)

@@ -51,6 +51,10 @@ struct FlatPlan {
     // reads (a generic pointer would make them flat loads, waited for with every load)
     lds_i32_ptr lens;
     bool has_lens;
+    // batch <= 64: every wave holds the whole batch, sequence b in lane b - its length,
+    // its flat work and its flat offset - so the plan needs no LDS and no barrier
+    bool wl;
+    int32_t lT, lw, lexcl;
     int32_t total;   // W
     int32_t big;     // positions per head unit
     int32_t n_big;   // head units: [u * big, (u + 1) * big) for u < n_big
@@ -75,9 +79,15 @@ __device__ __forceinline__ int32_t unit_of(const FlatPlan& f, int32_t x) {
     return x < f.xb ? div_nn(x, f.big) : f.n_big + div_nn(x - f.xb, f.small);
 }
 
-// Span of sequence b, from the plan's LDS copy of the lengths when it has one.
+// seq_lens[b] as the plan read it (b uniform across the wave).
+__device__ __forceinline__ int32_t plan_len(const DecodeParams& p, const FlatPlan& f, int b) {
+    if (f.wl) return __builtin_amdgcn_readlane(f.lT, b);
+    return f.has_lens ? f.lens[b] : p.seq_lens[b];
+}
+
+// Span of sequence b, from the lengths the plan holds.
 __device__ __forceinline__ SeqSpan plan_span(const DecodeParams& p, const FlatPlan& f, int b) {
-    return f.has_lens ? seq_span_of(p, f.lens[b]) : seq_span(p, b);
+    return seq_span_of(p, plan_len(p, f, b));
 }
 
 // Flat work of sequence b: attended positions x segments per sequence.
@@ -95,37 +105,60 @@ __device__ __forceinline__ FlatPlan plan_flat(const DecodeParams& p, int n_wg) {
     FlatPlan f;
     f.has_lens = false;  // read from seq_lens while the plan is made
     f.lens = (lds_i32_ptr)s_lens;
-    f.per = (p.batch + THREADS - 1) / THREADS;  // sequences per thread
-    f.b0 = tid * f.per;
-    int32_t mine = 0;
-    for (int k = 0; k < f.per; ++k) {
-        const int b = f.b0 + k;
-        if (b < p.batch) {
-            const int32_t T = p.seq_lens[b];
-            if (p.batch <= kLenCache) s_lens[b] = T;
-            mine += seq_span_of(p, T).count * p.segs_per_seq;
-        }
-    }
-    // inclusive scan over the wave, then across waves
     const int lane = tid & 63;
-    int32_t inc = mine;
+    int32_t total = 0;
+    f.wl = p.batch <= 64;
+    f.lT = f.lw = f.lexcl = 0;
+    if (f.wl) {
+        // one sequence per lane, the same in every wave: a scan over the wave
+        const int32_t T = lane < p.batch ? p.seq_lens[lane] : 0;
+        const int32_t w = lane < p.batch ? seq_span_of(p, T).count * p.segs_per_seq : 0;
+        int32_t inc = w;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int32_t y = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += y;
-    }
-    if (lane == 63) s_part[tid >> 6] = inc;
-    __syncthreads();  // s_part and s_lens are complete
-    f.has_lens = p.batch <= kLenCache;
-    int32_t before = 0, total = 0;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        f.lT = T;
+        f.lw = w;
+        f.lexcl = inc - w;
+        total = __builtin_amdgcn_readlane(inc, 63);
+        f.per = 0;
+        f.b0 = 0;
+        f.excl = 0;
+        f.mine = 0;
+    } else {
+        f.per = (p.batch + THREADS - 1) / THREADS;  // sequences per thread
+        f.b0 = tid * f.per;
+        int32_t mine = 0;
+        for (int k = 0; k < f.per; ++k) {
+            const int b = f.b0 + k;
+            if (b < p.batch) {
+                const int32_t T = p.seq_lens[b];
+                if (p.batch <= kLenCache) s_lens[b] = T;
+                mine += seq_span_of(p, T).count * p.segs_per_seq;
+            }
+        }
+        // inclusive scan over the wave, then across waves
+        int32_t inc = mine;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int32_t v = s_part[w];
-        before += w < (tid >> 6) ? v : 0;
-        total += v;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) s_part[tid >> 6] = inc;
+        __syncthreads();  // s_part and s_lens are complete
+        f.has_lens = p.batch <= kLenCache;
+        int32_t before = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int32_t v = s_part[w];
+            before += w < (tid >> 6) ? v : 0;
+            total += v;
+        }
+        f.excl = before + inc - mine;
+        f.mine = mine;
     }
-    f.excl = before + inc - mine;
-    f.mine = mine;
     f.total = total;
     // units_per_wg = 0: units of exactly min_chunk positions (forced unit lengths)
     const int32_t units = n_wg * p.units_per_wg;
@@ -165,6 +198,11 @@ struct SeqAt {
     int32_t off;
 };
 __device__ __forceinline__ SeqAt seq_at(const DecodeParams& p, const FlatPlan& f, int32_t x) {
+    if (f.wl) {  // the lane whose sequence holds x, found by a ballot in every wave
+        const uint64_t hit = __ballot(f.lw > 0 && f.lexcl <= x && x < f.lexcl + f.lw);
+        const int b = hit ? (int)__builtin_ctzll(hit) : 0;
+        return SeqAt{b, __builtin_amdgcn_readlane(f.lexcl, b)};
+    }
     __shared__ int32_t s_b;
     __shared__ int32_t s_off;
     __syncthreads();  // earlier readers of s_b / s_off are done
