@@ -25,9 +25,10 @@
 // The slot count is bounded by units + segments.
 //
 // Nothing here needs the host to know the lengths: each workgroup reads seq_lens
-// (a scan over the batch) before its first K/V load, and keeps them in LDS (batches
-// of up to kLenCache sequences), so finding a unit's pieces costs no further memory
-// round trip before the loads.
+// (a scan over the batch) before its first K/V load and keeps them - in the lanes of
+// every wave for batches of up to 64 sequences (no LDS, no barrier), else in LDS
+// (batches of up to kLenCache sequences) - so finding a unit's pieces costs no further
+// memory round trip before the loads.
 //
 // Flat indices are 32-bit: the host launches over batch ranges whose flat range is
 // at most kFlatMax (batch x segments x the longest attended set, whatever seq_lens
