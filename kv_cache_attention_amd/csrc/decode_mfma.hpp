@@ -164,6 +164,9 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
         load_k(j0 + cur * TILE, kc);
         load_v(j0 + cur * TILE, vr);
     }
+    // the thread index for everything that follows the first loads
+    const int tp = opaque(tid);
+    const int lrp = tp % 16, lqp = (tp % 64) / 16;
 
     // rows' new-token index (for the causal / window mask); padding rows act as the last
     int row_i[R];
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     u32x4 qreg[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-        const int idx = tid + k * MFMA_THREADS;
+        const int idx = tp + k * MFMA_THREADS;
         const int f = idx / 64, ll = idx % 64;
         const int qt = f / KS, ks = f % KS;
         const int n = row0 + qt * 16 + ll % 16;
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     // tile's loads as well, which the loop's first step needs anyway)
 #pragma unroll
     for (int k = 0; k < QPT; ++k)
-        if (tid + k * MFMA_THREADS < G::QFRAGS * 64) qsm[tid + k * MFMA_THREADS] = qreg[k];
+        if (tp + k * MFMA_THREADS < G::QFRAGS * 64) qsm[tp + k * MFMA_THREADS] = qreg[k];
     __syncthreads();  // Q^T and the tile counter are ready
     int32_t nxt = cur < n_tiles ? grab(cur) : n_tiles;
 
@@ -410,9 +413,9 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
 #pragma unroll
     for (int qt = 0; qt < R; ++qt) {
         const float lt = xsum_16_32(lsum[qt]);
-        if (lq == 0) {
-            sm_m[wave][qt * 16 + lr] = m[qt];
-            sm_l[wave][qt * 16 + lr] = lt;
+        if (lqp == 0) {
+            sm_m[wave][qt * 16 + lrp] = m[qt];
+            sm_l[wave][qt * 16 + lrp] = lt;
         }
     }
     __syncthreads();  // every wave is done with its V staging area
@@ -424,16 +427,16 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
 #pragma unroll
             for (int qt = 0; qt < R; ++qt) {
                 const f32x4 v = o[dt][qt];
-                *reinterpret_cast<float4*>(slot + (qt * 16 + lr) * OROW + dt * 16 + lq * 4) =
+                *reinterpret_cast<float4*>(slot + (qt * 16 + lrp) * OROW + dt * 16 + lqp * 4) =
                     float4{v[0], v[1], v[2], v[3]};
             }
     }
     static_assert(MFMA_WAVES == 4, "a float4 of weights per row");
-    if (tid < NQ) {
+    if (tp < NQ) {
         float mw[MFMA_WAVES], M = NEG_INF;
 #pragma unroll
         for (int w = 0; w < MFMA_WAVES; ++w) {
-            mw[w] = sm_m[w][tid];
+            mw[w] = sm_m[w][tp];
             M = fmaxf(M, mw[w]);
         }
         const float Mu = M == NEG_INF ? 0.0f : M;
@@ -441,12 +444,12 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
 #pragma unroll
         for (int w = 0; w < MFMA_WAVES; ++w) {
             e[w] = fast_exp2(mw[w] - Mu);  // 0 for a wave that saw nothing
-            L += sm_l[w][tid] * e[w];
+            L += sm_l[w][tp] * e[w];
         }
         // 8-bit caches: P.V was taken on raw codes, the V scale multiplies the rows
         const float inv = L > 0.0f ? (KT == FP8 ? p.v_scale[kvh] : 1.0f) / L : 0.0f;
-        sm_wt[tid] = float4{e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv};
-        sm_ml[tid] = float2{M, L};
+        sm_wt[tp] = float4{e[0] * inv, e[1] * inv, e[2] * inv, e[3] * inv};
+        sm_ml[tp] = float2{M, L};
     }
     __syncthreads();
     // rows out, four d at a time: the final rows (one piece) or this piece's partial.
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     float4 ca[CH][MFMA_WAVES];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-        const int idx = tid + k * MFMA_THREADS;
+        const int idx = tp + k * MFMA_THREADS;
         const int n = idx / (D / 4);
         const int d = (idx - n * (D / 4)) * 4;
         cw[k] = sm_wt[n];
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(MFMA_THREADS, R <= 3 ? KVATTN_MFMA_WG_PER_CU : 1) v
     }
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-        const int idx = tid + k * MFMA_THREADS;
+        const int idx = tp + k * MFMA_THREADS;
         const int n = idx / (D / 4);
         const int d = (idx - n * (D / 4)) * 4;
         if (row0 + n >= p.rows) continue;

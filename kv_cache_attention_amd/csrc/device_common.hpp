@@ -257,6 +257,16 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x, unknown to the optimiser from here on (an empty asm statement that claims to
+// change it): arithmetic on the result stays where the source puts it.  Per-thread
+// offsets used only after a piece's first loads (LDS slots, Q rows, the epilogue's
+// chunks) would otherwise be computed once ahead of the whole unit loop - before any
+// K/V load goes out, at one wave per SIMD - and held in registers (or spilled) across it.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // K/V stream loads: each cached byte is read once per step, so the loads carry the
 // nontemporal hint (global_load ... nt), which keeps the stream from displacing
 // cache lines other data still needs; measured on MI355X, plain reads of a 512 MiB
